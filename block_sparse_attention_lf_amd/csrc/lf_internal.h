@@ -1,0 +1,33 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host code of
+// liblf.so. Not part of the public interface (include/lf.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lf.h"
+
+namespace lf {
+
+// Geometry as the kernels see it: everything derived once on the host, plus
+// the slot table copied by value into the launch (no device copy needed).
+struct KGeom {
+  int32_t B, H, D, T, b, Fc, Fh, ns, S;
+  int32_t nb;   // blocks per frame = ceil(T / b)
+  int32_t nqb;  // query blocks = Fc * nb
+  int32_t Lq;   // queries = Fc * T
+  int32_t slot[LF_MAX_FRAMES];
+};
+
+// Launchers (one per kernel family). They assume validated arguments and
+// return the HIP error of the launch.
+hipError_t launch_compress(const KGeom& g, int32_t dtype, const void* q, const void* k_cache, float* q_blk, float* k_blk,
+                           float* k_frm, double* blk_sum, hipStream_t stream);
+hipError_t launch_select(const KGeom& g, const float* q_blk, const float* k_blk, const float* k_frm,
+                         int32_t kf, int32_t kb, int32_t k_frames_stride, int32_t* sel_frames,
+                         int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, hipStream_t stream);
+hipError_t launch_attention(const KGeom& g, int32_t dtype, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel, float scale,
+                            void* out, float* lse, hipStream_t stream);
+
+}  // namespace lf

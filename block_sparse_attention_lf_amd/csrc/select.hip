@@ -1,0 +1,124 @@
+// Two-stage mask selection for hierarchical sparse attention (Light Forcing,
+// technical summary 2.2 "two-stage mask selection"; press summary section 3):
+// per query block, rank the non-sink history frames by the inner product of
+// the pooled query with the frame-level keys, keep the top kf; inside each
+// kept frame rank its blocks by the block-level keys, keep the top kb. The
+// sink frames are attended in full. Output: ascending logical block ids.
+//
+// Numerics: scores are float64 dot products of the float32 pooled vectors
+// (every product is exact in float64), accumulated in ascending d. A
+// candidate is kept when fewer than k others rank above it, where c ranks
+// above c' if its score is larger, or equal with a lower index. That is
+// exactly "stable sort descending, take the first k" without sorting.
+//
+// Design: one wavefront per (batch, head, query block). Candidates map onto
+// lanes; each lane computes whole dot products (the pooled query is broadcast
+// from LDS), ranks are counted against the scores kept in LDS, and the kept
+// ids are compacted in ascending order with a ballot and a prefix popcount.
+// The whole step reads O(kf*nb + Fh) pooled vectors per query block,
+// independent of how long the history is beyond that.
+#include "lf_internal.h"
+
+namespace lf {
+namespace {
+
+template <int D>
+__device__ inline double dot_f64(const float* __restrict__ qv_lds, const float* __restrict__ k) {
+  double acc = 0.0;
+#pragma unroll 8
+  for (int d = 0; d < D; d += 4) {
+    const float4 kv = *reinterpret_cast<const float4*>(k + d);
+    acc = fma((double)qv_lds[d], (double)kv.x, acc);
+    acc = fma((double)qv_lds[d + 1], (double)kv.y, acc);
+    acc = fma((double)qv_lds[d + 2], (double)kv.z, acc);
+    acc = fma((double)qv_lds[d + 3], (double)kv.w, acc);
+  }
+  return acc;
+}
+
+// keep[c] = 1 iff fewer than k candidates rank above c.
+__device__ inline void rank_keep(const double* score, int n, int k, unsigned char* keep, int lane) {
+  for (int c = lane; c < n; c += 64) {
+    const double s = score[c];
+    int above = 0;
+    for (int i = 0; i < n; ++i) {
+      const double t = score[i];
+      above += (t > s) || (t == s && i < c);
+    }
+    keep[c] = above < k;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_blk, const float* __restrict__ k_blk,
+                                                    const float* __restrict__ k_frm, const KGeom g, int kf, int kb,
+                                                    int kf_stride, int32_t* __restrict__ sel_frames,
+                                                    int32_t* __restrict__ sel_blocks, int32_t* __restrict__ n_sel,
+                                                    int max_sel) {
+  __shared__ float qv[D];
+  __shared__ double fscore[LF_MAX_FRAMES];
+  __shared__ unsigned char fkeep[LF_MAX_FRAMES];
+  __shared__ double bscore[LF_MAX_BLOCKS_PER_FRAME];
+  __shared__ unsigned char bkeep[LF_MAX_BLOCKS_PER_FRAME];
+
+  const int lane = threadIdx.x;
+  const int64_t item = blockIdx.x;  // (b*H + h)*nqb + qb
+  const int64_t bh = item / g.nqb;
+  const int nb = g.nb, ns = g.ns;
+  for (int d = lane; d < D; d += 64) qv[d] = q_blk[item * D + d];
+  __syncthreads();
+
+  int32_t* out = sel_blocks + item * max_sel;
+  for (int i = lane; i < ns * nb; i += 64) out[i] = i;  // sink frames in full
+  int pos = ns * nb;
+
+  const int ncand = g.Fh - ns;
+  const float* frm = k_frm + (bh * g.Fh + ns) * D;
+  for (int c = lane; c < ncand; c += 64) fscore[c] = dot_f64<D>(qv, frm + (int64_t)c * D);
+  __syncthreads();
+  rank_keep(fscore, ncand, kf, fkeep, lane);
+  __syncthreads();
+
+  int nf = 0;
+  for (int c = 0; c < ncand; ++c) {
+    if (!fkeep[c]) continue;  // same value in every lane
+    const int f = ns + c;
+    if (sel_frames != nullptr && lane == 0 && nf < kf_stride) sel_frames[item * kf_stride + nf] = f;
+    ++nf;
+    const float* blk = k_blk + (bh * g.Fh + f) * (int64_t)nb * D;
+    for (int j = lane; j < nb; j += 64) bscore[j] = dot_f64<D>(qv, blk + (int64_t)j * D);
+    __syncthreads();
+    rank_keep(bscore, nb, kb, bkeep, lane);
+    __syncthreads();
+    for (int j0 = 0; j0 < nb; j0 += 64) {
+      const int j = j0 + lane;
+      const bool take = j < nb && bkeep[j];
+      const unsigned long long m = __ballot(take);
+      const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
+      if (take && at < max_sel) out[at] = f * nb + j;  // bound holds unless scores are NaN
+      pos = min(pos + __popcll(m), max_sel);
+    }
+    __syncthreads();  // bscore/bkeep are rewritten for the next kept frame
+  }
+  if (sel_frames != nullptr)
+    for (int i = nf + lane; i < kf_stride; i += 64) sel_frames[item * kf_stride + i] = -1;
+  for (int i = pos + lane; i < max_sel; i += 64) out[i] = -1;
+  if (lane == 0) n_sel[item] = pos;
+}
+
+}  // namespace
+
+hipError_t launch_select(const KGeom& g, const float* q_blk, const float* k_blk, const float* k_frm, int32_t kf,
+                         int32_t kb, int32_t k_frames_stride, int32_t* sel_frames, int32_t* sel_blocks,
+                         int32_t* n_sel, int32_t max_sel, hipStream_t stream) {
+  const unsigned grid = (unsigned)((int64_t)g.B * g.H * g.nqb);
+  if (g.D == 128)
+    hipLaunchKernelGGL((select_kernel<128>), dim3(grid), dim3(64), 0, stream, q_blk, k_blk, k_frm, g, kf, kb,
+                       k_frames_stride, sel_frames, sel_blocks, n_sel, max_sel);
+  else
+    hipLaunchKernelGGL((select_kernel<64>), dim3(grid), dim3(64), 0, stream, q_blk, k_blk, k_frm, g, kf, kb,
+                       k_frames_stride, sel_frames, sel_blocks, n_sel, max_sel);
+  return hipGetLastError();
+}
+
+}  // namespace lf

@@ -1,0 +1,190 @@
+/*
+ * lf.h -- C ABI of liblf.so, an MI355X (gfx950) implementation of Light
+ * Forcing's hierarchical sparse attention for chunk-wise autoregressive video
+ * diffusion, and of its chunk-aware sparsity budget.
+ *
+ * Source pages (cited by title and section):
+ *   [LF-tech]  "Light Forcing: Accelerating Autoregressive Video Diffusion via
+ *              Sparse Attention" (arXiv 2602.04789), technical summary:
+ *              2.1 chunk-aware growth (CAG), 2.2 hierarchical sparse attention
+ *              (HSA: token compression, two-stage mask selection, execution).
+ *   [LF-press] press summary of the same paper, section 3 (hierarchical
+ *              sparse attention) and section 2 (chunk-aware growth).
+ *   [SF]       Self Forcing news page, rolling KV cache paragraph.
+ *   [RF]       Rolling Forcing page, section 3, dual cache / attention anchor.
+ *
+ * Conventions shared by every entry point
+ *   - Geometry: a frame is `tokens_per_frame` (T) tokens. Every frame is cut
+ *     into nb = ceil(T / block) blocks; the last block of a frame holds the
+ *     remaining T - (nb-1)*block tokens. Blocks never straddle frames.
+ *     The current chunk has `chunk_frames` (Fc) frames, Lq = Fc*T queries and
+ *     nqb = Fc*nb query blocks (query block qb = frame qb/nb, block qb%nb).
+ *     The cache holds `hist_frames` (Fh) history frames; the first `n_sink`
+ *     of them are attention sinks (always attended in full, never ranked).
+ *   - Logical frames: 0..Fh-1 are the history (oldest first), Fh..Fh+Fc-1 the
+ *     current chunk. `frame_slot` is a HOST array of Fh+Fc int32 giving the
+ *     cache slot of each logical frame (distinct values in [0, cache_slots));
+ *     it is read during the call and copied into the launch, so the caller
+ *     may reuse it as soon as the call returns. This is how a rolling or an
+ *     anchored cache rotates without moving data.
+ *   - Logical block id of block j of history frame f: f*nb + j.
+ *   - Layouts (all row-major, contiguous, device memory):
+ *       q        [B, H, Lq, D]               dtype
+ *       k_cache  [B, H, cache_slots, T, D]   dtype (v_cache the same)
+ *       q_blk    [B, H, nqb, D]              float32
+ *       k_blk    [B, H, Fh*nb, D]            float32
+ *       k_frm    [B, H, Fh, D]               float32
+ *       out      [B, H, Lq, D]               dtype;  lse [B, H, Lq] float32
+ *     D (head_dim) is 64 or 128. dtype LF_BF16 or LF_F32. q, caches and out
+ *     must be 16-byte aligned.
+ *   - Ownership: every pointer is owned by the caller. The library never
+ *     allocates, frees or synchronises; device work is enqueued on `stream`
+ *     (a hipStream_t; NULL is the null stream) and the call returns at once.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued. A failing call returns a negative lf_status and enqueues
+ *     nothing. LF_ERR_HIP reports a launch failure; lf_last_error() gives the
+ *     detail string (per thread). There is no other global state.
+ */
+#ifndef LF_H_
+#define LF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LF_OK = 0,
+  LF_ERR_NULL = -1,      /* a required pointer is NULL */
+  LF_ERR_GEOM = -2,      /* geometry out of the supported range */
+  LF_ERR_DTYPE = -3,     /* unknown dtype */
+  LF_ERR_K = -4,         /* top-k sizes / selection capacity invalid */
+  LF_ERR_ALIGN = -5,     /* a device pointer is not 16-byte aligned */
+  LF_ERR_HIP = -6,       /* the HIP runtime rejected a launch */
+  LF_ERR_WORKSPACE = -7, /* workspace missing or too small */
+  LF_ERR_SLOT = -8,      /* frame_slot entry out of range or repeated */
+  LF_ERR_ARG = -9        /* another argument out of range */
+} lf_status;
+
+typedef enum { LF_F32 = 0, LF_BF16 = 1 } lf_dtype;
+
+typedef enum { LF_CACHE_ROLLING = 0, LF_CACHE_ANCHORED = 1 } lf_cache_policy;
+
+/* Most logical frames (Fh + Fc) one call may name. */
+#define LF_MAX_FRAMES 256
+/* Most blocks per frame (nb) the selection supports. */
+#define LF_MAX_BLOCKS_PER_FRAME 512
+/* Largest block (tokens) the attention kernel supports. */
+#define LF_MAX_BLOCK 128
+
+typedef struct {
+  int32_t batch;            /* B >= 1 */
+  int32_t heads;            /* H >= 1 */
+  int32_t head_dim;         /* D: 64 or 128 */
+  int32_t tokens_per_frame; /* T >= 1 */
+  int32_t block;            /* b: 1..LF_MAX_BLOCK */
+  int32_t chunk_frames;     /* Fc >= 1 */
+  int32_t hist_frames;      /* Fh >= 0; Fh + Fc <= LF_MAX_FRAMES */
+  int32_t n_sink;           /* 0 <= n_sink <= Fh */
+  int32_t cache_slots;      /* >= Fh + Fc */
+  int32_t dtype;            /* lf_dtype */
+} lf_geom;
+
+typedef void* lf_stream; /* hipStream_t */
+
+/* ---------------------------------------------------------------------------
+ * Token compression  ([LF-tech] 2.2 "token compression"; [LF-press] 3).
+ * Mean pooling: q_blk[qb] = mean of the query block's tokens; k_blk[f*nb+j] =
+ * mean of block j of history frame f; k_frm[f] = mean of all T tokens of
+ * history frame f. Means are accumulated in float64 and rounded once to
+ * float32 (mean = (float)(sum / count)).
+ * `workspace` (device, >= lf_compress_workspace_bytes(g) bytes, 8-byte
+ * aligned) holds the float64 block sums between the block and frame passes;
+ * it may be NULL only when that size is 0. Its contents on entry are ignored.
+ * ------------------------------------------------------------------------- */
+size_t lf_compress_workspace_bytes(const lf_geom* g);
+lf_status lf_compress(const lf_geom* g, const void* q, const void* k_cache, const int32_t* frame_slot,
+                      float* q_blk, float* k_blk, float* k_frm, void* workspace, size_t workspace_bytes,
+                      lf_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * Two-stage mask selection ([LF-tech] 2.2 "two-stage mask selection";
+ * [LF-press] 3). Per (batch, head, query block):
+ *   1. frame score s_f = <q_blk, k_frm[f]> in float64 for the non-sink
+ *      history frames; keep the kf = min(k_frames, Fh - n_sink) largest;
+ *   2. inside each kept frame, block score <q_blk, k_blk[f*nb+j]>; keep the
+ *      kb = min(k_blocks, nb) largest;
+ *   3. selected ids = all blocks of the sink frames + the kept (f, j),
+ *      ascending. Ties in either top-k go to the lower index.
+ * Outputs: sel_blocks [B,H,nqb,max_sel] int32 (ids ascending, then -1),
+ * n_sel [B,H,nqb] int32, and optionally (nullable) sel_frames
+ * [B,H,nqb,k_frames] int32 (kept frames ascending, then -1).
+ * max_sel must be >= lf_max_sel(g, k_frames, k_blocks). k_frames, k_blocks
+ * must be >= 0. The selected count never depends on Fh beyond the clamps.
+ * ------------------------------------------------------------------------- */
+int32_t lf_max_sel(const lf_geom* g, int32_t k_frames, int32_t k_blocks);
+lf_status lf_select(const lf_geom* g, const float* q_blk, const float* k_blk, const float* k_frm,
+                    int32_t k_frames, int32_t k_blocks, int32_t* sel_frames, int32_t* sel_blocks,
+                    int32_t* n_sel, int32_t max_sel, lf_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * Block-sparse attention ([LF-tech] 2.2 "execution"; [LF-press] 3).
+ * Each query row of query block qb attends, with softmax(scale * q k^T) v, to
+ * the tokens of the history blocks sel_blocks[qb][0 .. n_sel[qb]-1] and to
+ * every token of the current chunk (logical frames Fh..Fh+Fc-1; the chunk is
+ * denoised jointly, so its own tokens are all visible). Ids outside
+ * [0, Fh*nb) and entries at or beyond min(n_sel, max_sel) are ignored.
+ * Accumulation and the online softmax run in float32 on bf16 (or f32) MFMA
+ * products. out gets the normalised output in dtype; lse (nullable) the
+ * natural-log normaliser per query row.
+ * ------------------------------------------------------------------------- */
+lf_status lf_block_sparse_attn(const lf_geom* g, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* frame_slot, const int32_t* sel_blocks, const int32_t* n_sel,
+                               int32_t max_sel, float softmax_scale, void* out, float* lse, lf_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * Chunk-aware growth budget ([LF-tech] 2.1; [LF-press] 2). Host only.
+ * s_i = s_base - beta / sqrt(sigma_i) for the non-dense chunks, s_i = 0 for
+ * dense ones; beta makes the weight-weighted mean of s_i over the non-dense
+ * chunks equal s_target:
+ *   beta = (s_base - s_target) * sum w_i / sum (w_i / sqrt(sigma_i)).
+ * Top-k sizes of chunk i (Fi = hist_frames[i], ns = n_sink[i], nb blocks per
+ * frame): budget = (1 - s_i) * Fi * nb - ns * nb blocks beyond the sinks;
+ *   k_frames = min(Fi - ns, max(k_frames_min, ceil(budget / nb)))
+ *   k_blocks = min(nb, max(1, floor(budget / k_frames + 0.5)))
+ * (ceil with a 1e-9 allowance); 0 and 0 when there is nothing to select.
+ * A dense chunk gets k_frames = Fi - ns and k_blocks = nb (everything).
+ * weight and n_sink may be NULL (all 1 / all 0). sigma_i must be > 0.
+ * ------------------------------------------------------------------------- */
+lf_status lf_chunk_budget(int32_t n_chunks, const double* sigma, const double* weight, const uint8_t* dense,
+                          double s_base, double s_target, const int32_t* hist_frames, const int32_t* n_sink,
+                          int32_t blocks_per_frame, int32_t k_frames_min, double* sparsity_out,
+                          double* beta_out, int32_t* k_frames_out, int32_t* k_blocks_out);
+
+/* ---------------------------------------------------------------------------
+ * KV-cache slot table ([SF] rolling cache: keep the last frames, evict the
+ * oldest; [RF] dual cache: the first n_sink frames stay as an anchor). Host
+ * only. For the chunk with index `chunk_index` (its frames are absolute
+ * frames c*Fc .. c*Fc+Fc-1), returns the history kept next to it and the
+ * slot of every logical frame: absolute frame a lives in slot
+ *   rolling : a mod cache_slots
+ *   anchored: a if a < n_sink, else n_sink + (a - n_sink) mod (cache_slots - n_sink)
+ * The history is the newest frames that fit beside the current chunk (plus
+ * the anchors), oldest first. frame_slot_out needs cache_slots entries;
+ * frame_ids_out (nullable) gets the absolute frame of each logical frame.
+ * ------------------------------------------------------------------------- */
+lf_status lf_cache_frame_slots(int32_t policy, int32_t cache_slots, int32_t n_sink, int32_t chunk_frames,
+                               int32_t chunk_index, int32_t* hist_frames_out, int32_t* frame_slot_out,
+                               int32_t* frame_ids_out);
+
+/* Human-readable status name; the detail of the last failure on this thread. */
+const char* lf_status_str(lf_status s);
+const char* lf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LF_H_ */
