@@ -1,0 +1,256 @@
+"""Benchmark of one hierarchical sparse attention call per step on one MI355X.
+
+A step is the whole hot path for one (chunk, denoise step, layer): the cache
+slot table and chunk budget on the host, then lf_compress -> lf_select ->
+lf_block_sparse_attn on the GPU. The workload is the Wan-1.3B-like 480p chunk
+(12 heads, d=128, 1560 tokens per frame, 3 query frames, 6 history frames,
+64-token blocks, 80% sparsity, bf16). Inputs are synthetic, seeded, and
+resident in HBM before timing; four input sets (about 400 MB) rotate from
+step to step so each step reads its keys/values cold from HBM, as successive
+layers would.
+
+Prints one JSON line. ``value`` is effective attention TFLOP/s of the whole
+step (FLOPs actually needed on the selected blocks plus the current chunk,
+4*n_q*n_k*d over valid tokens, divided by the step time).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective attention TFLOP/s + % MFMA bf16 peak per 480p chunk; ms/chunk-layer"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+N_SETS = 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the 480p chunk)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-qblocks", type=int, default=0, help="0: every query block (the whole call)")
+    return ap.parse_args()
+
+
+def effective_flops(w, sel: np.ndarray, n_sel: np.ndarray) -> float:
+    """sum over (b, h, query block) of 4 * rows * keys * d, valid tokens only."""
+    T, b, nb, d = w.tokens_per_frame, w.block, w.blocks_per_frame, w.head_dim
+    blen = np.array([min(b, T - j * b) for j in range(nb)], np.int64)
+    qlen = np.tile(blen, w.chunk_frames)  # rows of each query block
+    total = 0.0
+    for bi in range(w.batch):
+        for h in range(w.heads):
+            for qb in range(w.n_qblocks):
+                ids = sel[bi, h, qb, :n_sel[bi, h, qb]]
+                keys = w.q_len + int(blen[ids % nb].sum())
+                total += 4.0 * qlen[qb] * keys * d
+    return total
+
+
+def compress_bytes(w) -> float:
+    """Algorithmic HBM bytes of lf_compress: read q and the history keys, write the pooled vectors."""
+    es = 2 if w.dtype == "bf16" else 4
+    B, H, d = w.batch, w.heads, w.head_dim
+    read = B * H * (w.q_len + w.hist_frames * w.tokens_per_frame) * d * es
+    write = B * H * (w.n_qblocks + w.hist_frames * w.blocks_per_frame + w.hist_frames) * d * 4
+    return float(read + write)
+
+
+def file_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_src: str, workload: str):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs, if they match this kernel."""
+    p = os.path.join(ROOT, "profiles", "attention_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != file_hash(kernel_src) or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, k_frames, k_blocks, sample_qblocks: int):
+    """The oracle, untuned, on the host cores: full compress + select, attention on a sample of query blocks."""
+    from oracle import lf_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    c = O.compress(x["q"], x["k_cache"], x["frame_slot"], w.tokens_per_frame, w.block, w.chunk_frames, w.hist_frames)
+    t1 = time.perf_counter()
+    s = O.select(c["q_blk"], c["k_blk"], c["k_frm"], w.hist_frames, w.n_sink, w.blocks_per_frame, k_frames, k_blocks)
+    t2 = time.perf_counter()
+    rng = np.random.default_rng(0)
+    all_q = [(b, h, qb) for b in range(w.batch) for h in range(w.heads) for qb in range(w.n_qblocks)]
+    n_pick = len(all_q) if sample_qblocks <= 0 else min(sample_qblocks, len(all_q))
+    pick = [all_q[i] for i in sorted(rng.choice(len(all_q), size=n_pick, replace=False))]
+    scale = 1.0 / math.sqrt(w.head_dim)
+    t3 = time.perf_counter()
+    O.attention(x["q"], x["k_cache"], x["v_cache"], x["frame_slot"], s["sel_blocks"], s["n_sel"], w.tokens_per_frame,
+                w.block, w.chunk_frames, w.hist_frames, scale, qblocks=pick)
+    t4 = time.perf_counter()
+    t_attn_full = (t4 - t3) * len(all_q) / len(pick)
+    t_step = (t1 - t0) + (t2 - t1) + t_attn_full
+    flops = effective_flops(w, s["sel_blocks"], s["n_sel"])
+    return {
+        "value": float(flops / t_step / 1e12), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"full oracle compress ({t1 - t0:.2f}s) + select ({t2 - t1:.2f}s) of one 480p chunk call; "
+                   f"float64 dense-masked attention on {len(pick)} of {len(all_q)} query blocks "
+                   f"({t4 - t3:.2f}s), scaled to all of them; {t_step:.1f}s per call"),
+        "s_per_step": t_step,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); per-GPU work shards by head with no exchange, see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_sparse_attention_lf_amd import inputs as I
+    from block_sparse_attention_lf_amd import lf
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = I.WORKLOADS[args.workload] if args.workload else I.WAN480P_CHUNK
+    g = lf.geom_of(w)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    print(f"[bench] workload {w.name}: drawing {N_SETS} input sets", file=sys.stderr, flush=True)
+
+    sets = []
+    host0 = None
+    for i in range(N_SETS):
+        x = I.make_inputs(w, seed=w.seed + 1000 * i)
+        if i == 0:
+            host0 = x
+        dev = tuple(torch.from_numpy(x[k]).to(tdt).cuda() for k in ("q", "k_cache", "v_cache"))
+        sets.append(dev)
+        if i > 0:
+            del x
+    set_bytes = sum(t.numel() * t.element_size() for t in sets[0])
+    bufs = lf.Buffers(g, w.k_frames, w.k_blocks)
+    stream = torch.cuda.current_stream()
+    policy = w.policy
+    n = 1
+
+    def host_side():
+        # a0: slot table of the cache for this chunk; a6: chunk budget (single call: its own sparsity)
+        hist, slots, _ = lf.lf_cache_frame_slots(policy, w.cache_slots, w.n_sink, w.chunk_frames, w.chunk_index)
+        lf.lf_chunk_budget([1.0], None, [False], w.sparsity, w.sparsity, [hist], [w.n_sink], w.blocks_per_frame,
+                           w.k_frames)
+        return slots
+
+    slots = host_side()
+    assert list(slots) == host0["frame_slot"].tolist()
+
+    # Effective FLOPs of each input set (selection is deterministic per set).
+    flops = []
+    for dev in sets:
+        lf.hsa_attention(g, *dev, slots, bufs, scale)
+        torch.cuda.synchronize()
+        flops.append(effective_flops(w, bufs.sel_blocks.cpu().numpy(), bufs.n_sel.cpu().numpy()))
+
+    def step(i, ev=None):
+        q, kc, vc = sets[i % N_SETS]
+        sl = host_side()
+        if ev is not None:
+            ev[0].record(stream)
+        lf.lf_compress(g, q, kc, sl, bufs.q_blk, bufs.k_blk, bufs.k_frm, bufs.workspace, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        lf.lf_select(g, bufs.q_blk, bufs.k_blk, bufs.k_frm, w.k_frames, w.k_blocks, bufs.sel_frames,
+                     bufs.sel_blocks, bufs.n_sel, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        lf.lf_block_sparse_attn(g, q, kc, vc, sl, bufs.sel_blocks, bufs.n_sel, scale, bufs.out, None, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps between two device synchronisations.
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / K
+    comp = [e[0].elapsed_time(e[1]) for e in evs]
+    sel = [e[1].elapsed_time(e[2]) for e in evs]
+    attn = [e[2].elapsed_time(e[3]) for e in evs]
+    flops_mean = float(np.mean([flops[i % N_SETS] for i in range(K)]))
+    attn_ms = float(np.mean(attn))
+    attn_tflops = flops_mean / (attn_ms * 1e-3) / 1e12
+    comp_ms = float(np.mean(comp))
+    cbytes = compress_bytes(w)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    value = flops_mean / (ms_step * 1e-3) / 1e12
+    src = os.path.join(ROOT, "block_sparse_attention_lf_amd", "csrc", "attention.hip")
+    traffic = traffic_from_profiles(src, w.name)
+
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": n, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1)/sqrt(d) q/k/v; no weights)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "tokens_per_frame": w.tokens_per_frame, "block": w.block, "chunk_frames": w.chunk_frames,
+                   "hist_frames": w.hist_frames, "k_frames": w.k_frames, "k_blocks": w.k_blocks,
+                   "sparsity": w.sparsity, "input_sets_rotated": N_SETS,
+                   "bytes_per_input_set": int(set_bytes)},
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel (lf_block_sparse_attn)",
+                     "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / peak, 4), "traffic": traffic,
+                     "algorithmic_flops_per_launch": flops_mean, "avg_launch_ms": round(attn_ms, 4)},
+        "stages_ms": {"compress": round(comp_ms, 4), "select": round(float(np.mean(sel)), 4),
+                      "attention": round(attn_ms, 4)},
+        "compress": {"bound": "hbm", "achieved_gbs": round(cbytes / (comp_ms * 1e-3) / 1e9, 1),
+                     "peak_gbs": PEAK_HBM_GBS, "frac": round(cbytes / (comp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": cbytes},
+        "attention_pct_of_mfma_peak": round(100 * attn_tflops / peak, 2),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cb = cpu_baseline(w, host0, w.k_frames, w.k_blocks, args.cpu_sample_qblocks)
+        cb.pop("s_per_step")
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
