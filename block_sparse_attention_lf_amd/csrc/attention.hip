@@ -4,27 +4,34 @@
 // current chunk, softmax(scale q k^T) v, with an fp32 online softmax.
 //
 // gfx950 design
-//   * One workgroup per (batch, head, query block); NW = ceil(block/32)
-//     wavefronts, each owning 32 query rows. Work is assigned XCD-aware: the
-//     hardware deals workgroups round-robin over the 8 XCDs, so workgroup w
-//     is remapped to work item p such that each XCD gets one contiguous range
-//     of (batch, head, query block) items. Query blocks of one head then run
-//     on one XCD and share the head's keys/values in that XCD's L2.
-//   * The key walk is a list of BN-key tiles: the current chunk frame by
-//     frame, then each selected history block (through the slot table).
-//     Tiles are staged in LDS, K row-major and V transposed, from registers
-//     that were prefetched from HBM while the previous tile was computed.
+//   * A workgroup owns 128 query rows: QPW consecutive query blocks of one
+//     (batch, head), WPQ = ceil(block/32) wavefronts per query block, 32 rows
+//     per wavefront (QPW = 4/WPQ). All its wavefronts share every key tile of
+//     the current chunk. For the history they walk the merged, ascending
+//     union of their query blocks' selected blocks: a tile is loaded once and
+//     only the wavefronts whose query block selected it compute on it, so no
+//     MFMA work is spent on unselected keys.
+//   * Work is dealt XCD-aware: the hardware hands workgroups round-robin to
+//     the 8 XCDs, so workgroup w is remapped such that each XCD gets one
+//     contiguous range of (batch, head, query-block group) items; query
+//     blocks of one head then share that head's keys/values in one L2.
+//   * Key/value tiles of BN=64 keys stream HBM -> LDS with global_load_lds
+//     (16 bytes per lane, no registers), double-buffered: tile t+1 is in
+//     flight while tile t is computed, one barrier per tile. Rows are stored
+//     row-major with the 16-byte chunks of row r XOR-swizzled by r, so the
+//     MFMA operand reads below are spread over the LDS banks. Rows past the
+//     end of a ragged tile load a copy of the last valid row (finite data,
+//     masked to -inf / weight 0), so no lane reads outside the cache.
 //   * MFMA 32x32x16 bf16 (32x32x2 f32 for fp32 inputs). Scores are formed
-//     transposed, S^T = K Q^T (A = K from LDS, B = Q kept in registers for
-//     the whole kernel), so that each lane ends up holding one query's
-//     scores; softmax statistics need only one cross-lane exchange (lane
-//     l and l^32), and the probabilities feed the next MFMA, O^T = V^T P^T,
-//     straight from registers as its B operand. V^T is written to LDS with
-//     the keys of each 16-key group permuted so that the A operand of every
-//     lane is one contiguous 16-byte LDS read.
-//   * exp2 with the scale folded into log2(e) units; masked (ragged) keys
-//     are -inf; rows past the end of a ragged query block are computed on
-//     zero queries and never stored.
+//     transposed, S^T = K Q^T (A = K from LDS, B = this wavefront's 32
+//     queries, kept in registers for the whole walk), so each lane holds one
+//     query's scores: the softmax needs one cross-lane exchange (lane l and
+//     l^32) and the probabilities are the B operand of O^T = V^T P^T straight
+//     from registers. The A operand V^T comes from the row-major V tile with
+//     ds_read_tr16_b64: inside each 16-lane group it hands lane i element
+//     i&3 of source lane 4e+(i>>2), i.e. four consecutive keys of one column.
+//   * exp2 with the scale folded into log2(e) units; rows past the end of a
+//     ragged query block are computed on zero queries and never stored.
 #include "lf_internal.h"
 
 namespace lf {
@@ -32,11 +39,14 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr float kLog2e = 1.4426950408889634f;
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-// Per-dtype MFMA traits.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int BN = 64;     // keys per tile
+
 template <typename T>
 struct Mma;
 
@@ -47,12 +57,6 @@ struct Mma<__bf16> {
   static __device__ inline f32x16 mfma(const frag& a, const frag& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  // LDS position of key `key` in a transposed V row: inside each group of
-  // 16 keys, key 8*a + 4*h + c goes to 8*h + 4*a + c, so that lane half h
-  // reads its 8 keys {8a + 4h + c} of one MFMA step as one 16-byte run.
-  static __device__ inline int vpos(int key) {
-    return (key & ~15) | ((key & 4) << 1) | ((key & 8) >> 1) | (key & 3);
-  }
 };
 
 template <>
@@ -62,313 +66,385 @@ struct Mma<float> {
   static __device__ inline f32x16 mfma(const frag& a, const frag& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
-  static __device__ inline int vpos(int key) { return key; }
 };
 
 // Key index held by accumulator register r of lane half h in a 32x32 MFMA
 // output (rows = keys): 8*(r/4) + 4*h + r%4.
 __device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-struct TileRef {
-  int64_t off;  // element offset of the tile's first key row in the cache
-  int count;    // valid keys in the tile (0: skip)
-};
+// Workgroups per CU to plan registers for: two for bf16 (their wavefronts
+// pair up on each SIMD, so one's softmax hides under the other's MFMAs);
+// fp32 inputs (small, correctness-oriented shapes) get the register file.
+template <typename T>
+constexpr int WG_PER_CU = sizeof(T) == 2 ? 2 : 1;
 
-template <typename T, int D, int NW, int BN>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(const T* __restrict__ q, const T* __restrict__ kc,
-                                                       const T* __restrict__ vc, const int32_t* __restrict__ sel,
-                                                       const int32_t* __restrict__ nsel, int max_sel, float scale,
-                                                       const KGeom g, T* __restrict__ out, float* __restrict__ lse) {
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 only.
+constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
+
+// One workgroup's walk: per-wavefront query fragments and accumulators, the
+// scalar tile producer, the LDS loader and the per-tile math.
+template <typename T, int D, int WPQ>
+struct Walk {
   using M = Mma<T>;
   using frag = typename M::frag;
-  constexpr int NT = NW * 64;
-  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  constexpr int CPR = D / EPC;              // chunks per key row
-  constexpr int KST = D + EPC;              // padded LDS row of K (elements)
-  constexpr int VST = BN + EPC;             // padded LDS row of V^T (elements)
-  constexpr int KTOT = BN * CPR;            // 16-byte K chunks per tile
-  constexpr int VTOT = (BN / 4) * CPR;      // V units (4 keys x 1 chunk) per tile
-  constexpr int KCH = (KTOT + NT - 1) / NT; // per thread
-  constexpr int VUN = (VTOT + NT - 1) / NT;
-  constexpr int QSTEPS = D / M::KSTEP;
-  constexpr int KH = BN / 32;               // 32-key halves per tile
-  constexpr int PSTEPS = BN / M::KSTEP;     // PV reduction steps per tile
-  constexpr int DB = D / 32;                // 32-wide output column blocks
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static constexpr int QPW = 4 / WPQ;              // query blocks per workgroup
+  static constexpr int NW = WPQ * QPW;             // wavefronts
+  static constexpr int NT = 64 * NW;
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int EPC = 16 / ES;              // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;              // chunks per key row
+  static constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;
+  static constexpr int TILE_CHUNKS = BN * CPR;
+  static constexpr int LI = (TILE_CHUNKS + NT - 1) / NT;  // load instructions per wavefront per tensor per tile
+  static constexpr int TILE_BYTES = BN * D * ES;
+  static constexpr int QSTEPS = D / M::KSTEP;
+  static constexpr int DB = D / 32;
+  static_assert(TILE_CHUNKS % 64 == 0, "whole load instructions");
 
-  __shared__ __attribute__((aligned(16))) T Ks[BN * KST];
-  __shared__ __attribute__((aligned(16))) T Vt[D * VST];
+  __device__ __forceinline__ explicit Walk(const KGeom& geom) : g(geom) {}
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-
-  // XCD-aware remap of the workgroup id to a work item.
-  const int nwg = gridDim.x, wg = blockIdx.x;
-  const int xcd = wg & 7, idx = wg >> 3, per = nwg >> 3, rem = nwg & 7;
-  const int item = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-  const int64_t bh = item / g.nqb;
-  const int qb = item - (int)bh * g.nqb;
-  const int fc = qb / g.nb, jq = qb - fc * g.nb;
-  const int64_t qrow0 = (int64_t)fc * g.T + (int64_t)jq * g.b;
-  const int nrows = min(g.b, g.T - jq * g.b);
-
-  // Queries of this wave (B operand of S^T = K Q^T), kept for the whole walk.
-  const int qr = wv * 32 + l32;
-  const bool wave_active = wv * 32 < nrows;
+  // geometry (a reference to the kernel argument: copying it would put the
+  // slot table in scratch memory) and identity
+  const KGeom& g;
+  const T* kc;
+  const T* vc;
+  int lane, wv, h, l32, lq, nrows, qr, qb0;
+  bool wave_active;
+  int64_t bh, qrow0;
+  // per-wavefront state
   frag qf[QSTEPS];
-  {
-    const T* qp = q + (bh * g.Lq + qrow0 + min(qr, nrows - 1)) * D;
-    const bool ok = qr < nrows;
+  f32x16 o[DB];
+  float m_run, l_run, c2;
+  // producer state (uniform)
+  const int32_t* lists;  // LDS copy, QPW rows of LF_MAX_SEL
+  int len[QPW], pos[QPW];
+  int tpf, n_cur, n_hist_blocks, all_mask, cur_next, hb_start, hb_end, hb_mask;
+  int64_t frame_elems, bh_base, hb_base;
+
+  // Next block of the merged ascending union of the lists (ids outside
+  // [0, Fh*nb) are skipped); false when every list is exhausted. Updates are
+  // branch-free so the list state stays in scalar registers.
+  __device__ __forceinline__ bool next_block(int& id_out, int& mask_out) {
+    for (;;) {
+      int id = INT32_MAX;
+      int hd[QPW];
 #pragma unroll
-    for (int s = 0; s < QSTEPS; ++s) {
-      if constexpr (sizeof(T) == 2) {
-        const uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + s * 16 + 8 * h) : make_uint4(0u, 0u, 0u, 0u);
-        qf[s] = __builtin_bit_cast(bf16x8, v);
-      } else {
-        qf[s] = ok ? qp[s * 2 + h] : 0.0f;
+      for (int i = 0; i < QPW; ++i) {
+        const int v = __builtin_amdgcn_readfirstlane(lists[i * LF_MAX_SEL + min(pos[i], LF_MAX_SEL - 1)]);
+        hd[i] = pos[i] < len[i] ? v : INT32_MAX;
+        id = min(id, hd[i]);
+      }
+      if (id == INT32_MAX) return false;
+      int mask = 0;
+#pragma unroll
+      for (int i = 0; i < QPW; ++i) {
+        const int hit = hd[i] == id;
+        mask |= hit << i;
+        pos[i] += hit;
+      }
+      if (id >= 0 && id < n_hist_blocks) {
+        id_out = id;
+        mask_out = mask;
+        return true;
       }
     }
   }
 
-  // Key walk: Fc frames of the current chunk (tiles of BN keys), then the
-  // selected history blocks (tiles of up to BN keys inside each block).
-  const int tpf = (g.T + BN - 1) / BN;
-  const int tpb = (g.b + BN - 1) / BN;
-  const int n_cur = g.Fc * tpf;
-  const int64_t sel_row = bh * g.nqb + qb;
-  const int nsel_q = max_sel > 0 ? min(max(nsel[sel_row], 0), max_sel) : 0;
-  const int32_t* my_sel = sel + sel_row * max_sel;
-  const int n_tiles = n_cur + nsel_q * tpb;
-  const int n_hist_blocks = g.Fh * g.nb;
-  const int64_t frame_elems = (int64_t)g.T * D;
-  const int64_t bh_base = bh * g.S * frame_elems;
+  // Fills (off, count, mask) of the next tile: the current chunk's tiles,
+  // then the union's history blocks (tiles of up to BN keys inside each);
+  // false when the walk is over. The counters advance with selects, not in
+  // separate branches, so that the compiler keeps them in registers.
+  __device__ __forceinline__ bool produce(int64_t& off, int& count, int& mask) {
+    const bool is_cur = cur_next < n_cur;
+    if (!is_cur && hb_start >= hb_end) {
+      int id, m;
+      if (!next_block(id, m)) return false;
+      const int f = id / g.nb, j = id - f * g.nb;
+      hb_mask = m;
+      hb_start = j * g.b;
+      hb_end = min(hb_start + g.b, g.T);
+      hb_base = bh_base + g.slot[f] * frame_elems;
+    }
+    const int cf = min(cur_next, n_cur - 1) / tpf;
+    const int c_start = (min(cur_next, n_cur - 1) - cf * tpf) * BN;
+    const int64_t c_off = bh_base + g.slot[g.Fh + cf] * frame_elems + (int64_t)c_start * D;
+    off = is_cur ? c_off : hb_base + (int64_t)hb_start * D;
+    count = is_cur ? min(BN, g.T - c_start) : min(BN, hb_end - hb_start);
+    mask = is_cur ? all_mask : hb_mask;
+    cur_next += is_cur ? 1 : 0;
+    hb_start += is_cur ? 0 : BN;
+    return true;
+  }
 
-  auto tile_ref = [&](int t) -> TileRef {
-    TileRef r;
-    if (t < n_cur) {
-      const int f = t / tpf, tt = t - f * tpf;
-      const int start = tt * BN;
-      r.count = min(BN, g.T - start);
-      r.off = bh_base + g.slot[g.Fh + f] * frame_elems + (int64_t)start * D;
-    } else {
-      const int u = t - n_cur, s = u / tpb, sub = u - s * tpb;
-      const int id = my_sel[s];
-      if (id < 0 || id >= n_hist_blocks) {
-        r.count = 0;
-        r.off = 0;
-      } else {
-        const int f = id / g.nb, j = id - f * g.nb;
-        const int bstart = j * g.b, bend = min(bstart + g.b, g.T);
-        const int start = bstart + sub * BN;
-        r.count = max(0, min(BN, bend - start));
-        r.off = bh_base + g.slot[f] * frame_elems + (int64_t)start * D;
+  // All wavefronts stream one tile (K and V) into a stage buffer.
+  __device__ __forceinline__ void issue(char* kd, char* vd, int64_t off, int count) {
+#pragma unroll
+    for (int i = 0; i < LI; ++i) {
+      const int L0 = (i * NW + wv) * 64;
+      if (TILE_CHUNKS % NT == 0 || L0 < TILE_CHUNKS) {
+        const int L = L0 + lane;
+        const int row = L / CPR, pc = L - row * CPR;
+        const int c = pc ^ (row & SWM);
+        const int64_t src = off + (int64_t)min(row, count - 1) * D + c * EPC;
+        __builtin_amdgcn_global_load_lds(kc + src, LDS_PTR(void, kd + L0 * 16), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vc + src, LDS_PTR(void, vd + L0 * 16), 16, 0, 0);
       }
     }
-    return r;
-  };
-  auto next_tile = [&](int t) {
-    while (t < n_tiles && tile_ref(t).count == 0) ++t;
-    return t;
-  };
+  }
 
-  uint4 kreg[KCH];
-  uint4 vreg[VUN][4];
-  auto load_tile = [&](const TileRef& r) {
+  // One tile on the stage (ks, vs): S^T, online softmax, O^T += V^T P^T.
+  __device__ __forceinline__ void compute(const char* ks, const char* vs, int count) {
+    f32x16 s[2];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * NT, row = c / CPR, cc = c - row * CPR;
-      kreg[i] = (KTOT % NT == 0 || c < KTOT) && row < r.count
-                    ? *reinterpret_cast<const uint4*>(kc + r.off + (int64_t)row * D + cc * EPC)
-                    : make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int kh = 0; kh < 2; ++kh) {
+      const int row = kh * 32 + l32;
+      const char* krow = ks + row * CPR * 16;
+      frag kf[QSTEPS];
 #pragma unroll
-    for (int i = 0; i < VUN; ++i) {
-      const int u = tid + i * NT, quad = u / CPR, cc = u - quad * CPR;
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const int row = quad * 4 + k4;
-        vreg[i][k4] = (VTOT % NT == 0 || u < VTOT) && row < r.count
-                          ? *reinterpret_cast<const uint4*>(vc + r.off + (int64_t)row * D + cc * EPC)
-                          : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * NT, row = c / CPR, cc = c - row * CPR;
-      if (KTOT % NT == 0 || c < KTOT) *reinterpret_cast<uint4*>(&Ks[row * KST + cc * EPC]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VUN; ++i) {
-      const int u = tid + i * NT, quad = u / CPR, cc = u - quad * CPR;
-      if (VTOT % NT != 0 && u >= VTOT) continue;
-      const int p0 = M::vpos(quad * 4);  // 4 consecutive keys stay consecutive
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const int wi = e >> 1;
-          uint32_t lo, hi;
-          if (e & 1) {
-            lo = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-            hi = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-          } else {
-            lo = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-            hi = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-          }
-          *reinterpret_cast<uint2*>(&Vt[(cc * EPC + e) * VST + p0]) = make_uint2(lo, hi);
-        }
-      } else {
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e)
-          *reinterpret_cast<uint4*>(&Vt[(cc * EPC + e) * VST + p0]) = make_uint4(w0[e], w1[e], w2[e], w3[e]);
-      }
-    }
-  };
-
-  f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
-  const float c2 = scale * kLog2e;
-
-  int t = next_tile(0);
-  TileRef cur = tile_ref(t < n_tiles ? t : 0);
-  if (t < n_tiles) load_tile(cur);
-  while (t < n_tiles) {
-    __syncthreads();  // every wave is done with the previous tile in LDS
-    store_tile();
-    __syncthreads();
-    const int tn = next_tile(t + 1);
-    TileRef nxt = cur;
-    if (tn < n_tiles) {
-      nxt = tile_ref(tn);
-      load_tile(nxt);  // in flight while this tile is computed
-    }
-    if (wave_active) {
-      // S^T = K Q^T, 32 keys x 32 queries per accumulator.
-      f32x16 s[KH];
-#pragma unroll
-      for (int kh = 0; kh < KH; ++kh) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kh][r] = 0.0f;
-        const T* krow = &Ks[(kh * 32 + l32) * KST];
-#pragma unroll
-        for (int st = 0; st < QSTEPS; ++st) {
-          frag a;
-          if constexpr (sizeof(T) == 2)
-            a = *reinterpret_cast<const bf16x8*>(krow + st * 16 + 8 * h);
-          else
-            a = krow[st * 2 + h];
-          s[kh] = M::mfma(a, qf[st], s[kh]);
-        }
-      }
-      if (cur.count < BN) {
-#pragma unroll
-        for (int kh = 0; kh < KH; ++kh)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kh * 32 + acc_row(r, h) >= cur.count) s[kh][r] = -INFINITY;
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kh = 0; kh < KH; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kh][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-      const float mc = m_new * c2;
-      float psum = 0.0f;
-#pragma unroll
-      for (int kh = 0; kh < KH; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kh][r], c2, -mc));
-          s[kh][r] = p;
-          psum += p;
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int ps = 0; ps < PSTEPS; ++ps) {
-        frag b;
-        if constexpr (sizeof(T) == 2) {
-          const int kh = ps >> 1, r0 = (ps & 1) * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) b[e] = (__bf16)s[kh][r0 + e];
+      for (int t = 0; t < QSTEPS; ++t) {
+        if constexpr (ES == 2) {
+          const int c = 2 * t + h;
+          kf[t] = *reinterpret_cast<const bf16x8*>(krow + ((c ^ (row & SWM)) * 16));
         } else {
-          b = s[ps >> 4][ps & 15];
+          const int d = 2 * t + h, c = d >> 2;
+          kf[t] = *reinterpret_cast<const float*>(krow + ((c ^ (row & SWM)) * 16) + 4 * (d & 3));
         }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kh][r] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < QSTEPS; ++t) s[kh] = M::mfma(kf[t], qf[t], s[kh]);
+    }
+    if (count < BN) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kh * 32 + acc_row(r, h) >= count) s[kh][r] = -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kh][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+    const float mc = m_new * c2;
+    float psum = 0.0f;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kh][r], c2, -mc));
+        s[kh][r] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+
+    if constexpr (ES == 2) {
+      const int grp = lane >> 4, s16 = lane & 15;
+#pragma unroll
+      for (int ps = 0; ps < BN / 16; ++ps) {
+        bf16x8 b;
+        const int kh = ps >> 1, r0 = (ps & 1) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = (__bf16)s[kh][r0 + e];
+        bf16x8 a[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const T* vrow = &Vt[(db * 32 + l32) * VST];
-          frag a;
-          if constexpr (sizeof(T) == 2)
-            a = *reinterpret_cast<const bf16x8*>(vrow + ps * 16 + 8 * h);
-          else
-            a = vrow[M::vpos((ps >> 4) * 32 + acc_row(ps & 15, h))];
+          const int col = 32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
+          const int c = col >> 3, byte = (col & 7) * 2;
+          i16x4 part[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int key = 16 * ps + 8 * j + 4 * h + (s16 >> 2);
+            part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                LDS_PTR(i16x4, vs + (key * CPR + (c ^ (key & SWM))) * 16 + byte));
+          }
+          a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = M::mfma(a[db], b, o[db]);
+      }
+    } else {
+#pragma unroll
+      for (int ps = 0; ps < BN / 2; ++ps) {
+        const int kh = ps >> 4, r = ps & 15;
+        const float b = s[kh][r];
+        const int key = kh * 32 + acc_row(r, h);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int dcol = 32 * db + l32;
+          const float a = *reinterpret_cast<const float*>(vs + (key * CPR + ((dcol >> 2) ^ (key & SWM))) * 16 +
+                                                          4 * (dcol & 3));
           o[db] = M::mfma(a, b, o[db]);
         }
       }
     }
-    t = tn;
-    cur = nxt;
+  }
+};
+
+template <typename T, int D, int WPQ>
+__global__ __launch_bounds__(64 * WPQ * (4 / WPQ), WG_PER_CU<T>) void attn_kernel(
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ nsel, int max_sel, float scale, const KGeom g, T* __restrict__ out,
+    float* __restrict__ lse) {
+  using W = Walk<T, D, WPQ>;
+  constexpr int QPW = W::QPW, NT = W::NT, ES = W::ES, QSTEPS = W::QSTEPS, DB = W::DB;
+
+  // Two named stage buffers (not one indexed array): the loop below is
+  // unrolled by two so every LDS read names its buffer at compile time, which
+  // lets the compiler see that reading one stage never waits on the DMA that
+  // is filling the other.
+  __shared__ __attribute__((aligned(1024))) char k0[W::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0[W::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1[W::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1[W::TILE_BYTES];
+  // The selected-block lists of this workgroup's query blocks, copied once.
+  __shared__ int32_t lists[QPW * LF_MAX_SEL];
+
+  W w(g);
+  w.kc = kc;
+  w.vc = vc;
+  const int tid = threadIdx.x;
+  w.lane = tid & 63;
+  w.wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  w.h = w.lane >> 5;
+  w.l32 = w.lane & 31;
+
+  // XCD-aware remap of the workgroup id to a work item (bh, query-block group).
+  const int nwg = gridDim.x, wg = blockIdx.x;
+  const int xcd = wg & 7, idx = wg >> 3, per = nwg >> 3, rem = nwg & 7;
+  const int item = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  const int groups = (g.nqb + QPW - 1) / QPW;
+  w.bh = item / groups;
+  w.qb0 = (item - (int)w.bh * groups) * QPW;
+
+  // This wavefront's query block and rows.
+  w.lq = w.wv / WPQ;
+  const int rg = w.wv - w.lq * WPQ;
+  const int qb = w.qb0 + w.lq;
+  const int fc = qb / g.nb, jq = qb - fc * g.nb;
+  w.nrows = qb < g.nqb ? min(g.b, g.T - jq * g.b) : 0;
+  w.qr = rg * 32 + w.l32;
+  w.wave_active = rg * 32 < w.nrows;
+  w.qrow0 = (int64_t)fc * g.T + (int64_t)jq * g.b;
+  {
+    const bool ok = w.qr < w.nrows;
+    const T* qp = q + (w.bh * g.Lq + w.qrow0 + (ok ? w.qr : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < QSTEPS; ++s) {
+      if constexpr (ES == 2) {
+        const uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + s * 16 + 8 * w.h) : make_uint4(0u, 0u, 0u, 0u);
+        w.qf[s] = __builtin_bit_cast(bf16x8, v);
+      } else {
+        w.qf[s] = ok ? qp[s * 2 + w.h] : 0.0f;
+      }
+    }
   }
 
-  if (!wave_active || qr >= nrows) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // Producer state.
+  w.tpf = (g.T + BN - 1) / BN;
+  w.n_cur = g.Fc * w.tpf;
+  w.n_hist_blocks = g.Fh * g.nb;
+  w.frame_elems = (int64_t)g.T * D;
+  w.bh_base = w.bh * g.S * w.frame_elems;
+  w.all_mask = (1 << min(QPW, g.nqb - w.qb0)) - 1;
+  w.lists = lists;
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int qbi = w.qb0 + i;
+    const int64_t row = w.bh * g.nqb + qbi;
+    w.len[i] = (qbi < g.nqb && max_sel > 0) ? __builtin_amdgcn_readfirstlane(min(max(nsel[row], 0), max_sel)) : 0;
+    w.pos[i] = 0;
+    for (int j = tid; j < w.len[i]; j += NT) lists[i * LF_MAX_SEL + j] = sel[row * max_sel + j];
+  }
+  __syncthreads();
+  w.cur_next = 0;
+  w.hb_start = w.hb_end = w.hb_mask = 0;
+  w.hb_base = 0;
+
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w.o[db][r] = 0.0f;
+  w.m_run = -INFINITY;
+  w.l_run = 0.0f;
+  w.c2 = scale * kLog2e;
+
+  // Double-buffered walk, unrolled by two so each half names its buffers.
+  int64_t noff = 0;
+  int ncount = 0, nmask = 0;
+  bool have = w.produce(noff, ncount, nmask);
+  if (have) w.issue(k0, v0, noff, ncount);
+  while (have) {
+    {
+      const int count = ncount, mask = nmask;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wavefront's share of the tile has landed
+      __syncthreads();                       // ... everyone's, and the other buffer is free
+      have = w.produce(noff, ncount, nmask);
+      if (have) w.issue(k1, v1, noff, ncount);
+      if (w.wave_active && ((mask >> w.lq) & 1)) w.compute(k0, v0, count);
+    }
+    if (!have) break;
+    {
+      const int count = ncount, mask = nmask;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      have = w.produce(noff, ncount, nmask);
+      if (have) w.issue(k0, v0, noff, ncount);
+      if (w.wave_active && ((mask >> w.lq) & 1)) w.compute(k1, v1, count);
+    }
+  }
+
+  if (!w.wave_active || w.qr >= w.nrows) return;
+  const float l_tot = w.l_run + __shfl_xor(w.l_run, 32);
   const float inv = 1.0f / l_tot;
-  T* orow = out + (bh * g.Lq + qrow0 + qr) * D;
+  T* orow = out + (w.bh * g.Lq + w.qrow0 + w.qr) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-      const int col = db * 32 + 8 * a4 + 4 * h;
-      if constexpr (sizeof(T) == 2) {
+      const int col = db * 32 + 8 * a4 + 4 * w.h;
+      if constexpr (ES == 2) {
         bf16x4 v;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = (__bf16)(o[db][a4 * 4 + c] * inv);
+        for (int c = 0; c < 4; ++c) v[c] = (__bf16)(w.o[db][a4 * 4 + c] * inv);
         *reinterpret_cast<bf16x4*>(orow + col) = v;
       } else {
-        *reinterpret_cast<float4*>(orow + col) =
-            make_float4(o[db][a4 * 4] * inv, o[db][a4 * 4 + 1] * inv, o[db][a4 * 4 + 2] * inv, o[db][a4 * 4 + 3] * inv);
+        *reinterpret_cast<float4*>(orow + col) = make_float4(w.o[db][a4 * 4] * inv, w.o[db][a4 * 4 + 1] * inv,
+                                                             w.o[db][a4 * 4 + 2] * inv, w.o[db][a4 * 4 + 3] * inv);
       }
     }
-  if (lse != nullptr && h == 0) lse[bh * g.Lq + qrow0 + qr] = m_run * scale + logf(l_tot);
+  if (lse != nullptr && w.h == 0) lse[w.bh * g.Lq + w.qrow0 + w.qr] = w.m_run * scale + logf(l_tot);
 }
 
-template <typename T, int D, int NW, int BN>
+template <typename T, int D, int WPQ>
 hipError_t launch_typed(const KGeom& g, const void* q, const void* k, const void* v, const int32_t* sel,
                         const int32_t* nsel, int max_sel, float scale, void* out, float* lse, hipStream_t stream) {
-  const unsigned grid = (unsigned)((int64_t)g.B * g.H * g.nqb);
-  hipLaunchKernelGGL((attn_kernel<T, D, NW, BN>), dim3(grid), dim3(NW * 64), 0, stream, static_cast<const T*>(q),
-                     static_cast<const T*>(k), static_cast<const T*>(v), sel, nsel, max_sel, scale, g,
-                     static_cast<T*>(out), lse);
+  constexpr int QPW = 4 / WPQ;
+  const unsigned grid = (unsigned)((int64_t)g.B * g.H * ((g.nqb + QPW - 1) / QPW));
+  hipLaunchKernelGGL((attn_kernel<T, D, WPQ>), dim3(grid), dim3(64 * WPQ * QPW), 0, stream,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sel, nsel, max_sel,
+                     scale, g, static_cast<T*>(out), lse);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_d(const KGeom& g, const void* q, const void* k, const void* v, const int32_t* sel,
                     const int32_t* nsel, int max_sel, float scale, void* out, float* lse, hipStream_t stream) {
-  if (g.b <= 32) return launch_typed<T, D, 1, 32>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
-  if (g.b <= 64) return launch_typed<T, D, 2, 64>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
-  return launch_typed<T, D, 4, 64>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
+  switch ((g.b + 31) / 32) {
+    case 1: return launch_typed<T, D, 1>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
+    case 2: return launch_typed<T, D, 2>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
+    case 3: return launch_typed<T, D, 3>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
+    default: return launch_typed<T, D, 4>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
+  }
 }
 
 }  // namespace

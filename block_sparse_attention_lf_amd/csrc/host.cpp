@@ -159,7 +159,7 @@ lf_status lf_block_sparse_attn(const lf_geom* g, const void* q, const void* k_ca
   if (st != LF_OK) return st;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr)
     return fail(LF_ERR_NULL, "q / k_cache / v_cache / out is NULL");
-  if (max_sel < 0) return fail(LF_ERR_K, "max_sel must be >= 0");
+  if (max_sel < 0 || max_sel > LF_MAX_SEL) return fail(LF_ERR_K, "max_sel must be in [0, LF_MAX_SEL]");
   if (max_sel > 0 && (sel_blocks == nullptr || n_sel == nullptr))
     return fail(LF_ERR_NULL, "sel_blocks / n_sel is NULL");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))

@@ -78,6 +78,8 @@ typedef enum { LF_CACHE_ROLLING = 0, LF_CACHE_ANCHORED = 1 } lf_cache_policy;
 #define LF_MAX_BLOCKS_PER_FRAME 512
 /* Largest block (tokens) the attention kernel supports. */
 #define LF_MAX_BLOCK 128
+/* Most selected blocks per query block the attention kernel reads (max_sel). */
+#define LF_MAX_SEL 512
 
 typedef struct {
   int32_t batch;            /* B >= 1 */
@@ -135,7 +137,9 @@ lf_status lf_select(const lf_geom* g, const float* q_blk, const float* k_blk, co
  * the tokens of the history blocks sel_blocks[qb][0 .. n_sel[qb]-1] and to
  * every token of the current chunk (logical frames Fh..Fh+Fc-1; the chunk is
  * denoised jointly, so its own tokens are all visible). Ids outside
- * [0, Fh*nb) and entries at or beyond min(n_sel, max_sel) are ignored.
+ * [0, Fh*nb) and entries at or beyond min(n_sel, max_sel) are ignored; the
+ * ids of one query block must be distinct (lf_select's are, and ascending).
+ * max_sel (the row stride of sel_blocks) must be <= LF_MAX_SEL.
  * Accumulation and the online softmax run in float32 on bf16 (or f32) MFMA
  * products. out gets the normalised output in dtype; lse (nullable) the
  * natural-log normaliser per query row.
