@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--workload", default=None, help="workload name (default: the 480p chunk)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-qblocks", type=int, default=0, help="0: every query block (the whole call)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run one elementwise kernel that reads and writes this many MiB "
+                         "(a known-size reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -244,6 +247,14 @@ def main():
                      "algorithmic_bytes": cbytes},
         "attention_pct_of_mfma_peak": round(100 * attn_tflops / peak, 2),
     }
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # reads and writes exactly n bf16 values
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes_each_way"] = n * 2
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, host0, w.k_frames, w.k_blocks, args.cpu_sample_qblocks)

@@ -68,6 +68,16 @@ struct Mma<float> {
   }
 };
 
+// A wave-uniform pointer moved to scalar registers (so address arithmetic on
+// it stays scalar and loads can use the scalar-base form).
+template <typename P>
+__device__ inline P* uniform_ptr(P* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+
 // Key index held by accumulator register r of lane half h in a 32x32 MFMA
 // output (rows = keys): 8*(r/4) + 4*h + r%4.
 __device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -177,17 +187,31 @@ struct Walk {
   }
 
   // All wavefronts stream one tile (K and V) into a stage buffer.
+  // This lane's chunk of every load instruction: its key row inside the tile
+  // and its byte offset from the tile's first row (swizzle applied).
+  int drow[LI];
+  uint32_t doff[LI];
+  __device__ __forceinline__ void init_loads() {
+#pragma unroll
+    for (int i = 0; i < LI; ++i) {
+      const int L = (i * NW + wv) * 64 + lane;
+      const int row = L / CPR, pc = L - row * CPR;
+      drow[i] = row;
+      doff[i] = (uint32_t)((row * D + (pc ^ (row & SWM)) * EPC) * ES);
+    }
+  }
+  // Rows past `count` re-read row count-1. The base is uniform and the lane
+  // offset 32-bit, so each load is one scalar-base DMA instruction.
   __device__ __forceinline__ void issue(char* kd, char* vd, int64_t off, int count) {
+    const char* kb = uniform_ptr(reinterpret_cast<const char*>(kc + off));
+    const char* vb = uniform_ptr(reinterpret_cast<const char*>(vc + off));
 #pragma unroll
     for (int i = 0; i < LI; ++i) {
       const int L0 = (i * NW + wv) * 64;
       if (TILE_CHUNKS % NT == 0 || L0 < TILE_CHUNKS) {
-        const int L = L0 + lane;
-        const int row = L / CPR, pc = L - row * CPR;
-        const int c = pc ^ (row & SWM);
-        const int64_t src = off + (int64_t)min(row, count - 1) * D + c * EPC;
-        __builtin_amdgcn_global_load_lds(kc + src, LDS_PTR(void, kd + L0 * 16), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vc + src, LDS_PTR(void, vd + L0 * 16), 16, 0, 0);
+        const uint32_t o = count == BN ? doff[i] : doff[i] - (uint32_t)((drow[i] - min(drow[i], count - 1)) * D * ES);
+        __builtin_amdgcn_global_load_lds(kb + o, LDS_PTR(void, kd + L0 * 16), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + o, LDS_PTR(void, vd + L0 * 16), 16, 0, 0);
       }
     }
   }
@@ -228,9 +252,20 @@ struct Walk {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kh][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
+    // Lazy rescale: the reference max moves (and O, l are rescaled) only when
+    // some row's max grew by more than 8 in log2 units; otherwise the stale
+    // max stays, every p <= 2^8, and the softmax is unchanged in exact math.
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-    const float mc = m_new * c2;
+    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c2 > 8.0f) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    const float mc = m_run * c2;
     float psum = 0.0f;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -240,12 +275,7 @@ struct Walk {
         s[kh][r] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    l_run += psum;
 
     if constexpr (ES == 2) {
       const int grp = lane >> 4, s16 = lane & 15;
@@ -367,6 +397,7 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), WG_PER_CU<T>) void attn_kerne
   }
   __syncthreads();
   w.cur_next = 0;
+  w.init_loads();
   w.hb_start = w.hb_end = w.hb_mask = 0;
   w.hb_base = 0;
 

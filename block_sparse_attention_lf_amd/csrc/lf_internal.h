@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/lf.h"
+#include "lf.h"
 
 namespace lf {
 
