@@ -133,7 +133,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}); per-GPU work shards by head with no exchange, see the design notes.",
+              f"WORLD_SIZE={world}); split over GPUs, the work would shard by head with no exchange.",
               file=sys.stderr)
         sys.exit(2)
 
