@@ -101,15 +101,20 @@ struct Walk {
   static constexpr int NW = WPQ * QPW;             // wavefronts
   static constexpr int NT = 64 * NW;
   static constexpr int ES = (int)sizeof(T);
-  static constexpr int EPC = 16 / ES;              // elements per 16-byte chunk
-  static constexpr int CPR = D / EPC;              // chunks per key row
-  static constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;
-  static constexpr int TILE_CHUNKS = BN * CPR;
-  static constexpr int LI = (TILE_CHUNKS + NT - 1) / NT;  // load instructions per wavefront per tensor per tile
-  static constexpr int TILE_BYTES = BN * D * ES;
+  static constexpr int CPR = D * ES / 16;          // 16-byte chunks per key row
+  // LDS rows are padded by 32 bytes: consecutive rows then start 32 bytes
+  // apart modulo the 256-byte bank cycle, so eight 16-byte K reads of eight
+  // rows, and the four 32-byte row pieces a transposing V read gathers, all
+  // land on distinct banks; and every fragment address is one per-lane base
+  // plus a compile-time offset.
+  static constexpr int RS = D * ES + 32;           // LDS row stride in bytes
+  static constexpr int SPR = RS / 16;              // 16-byte slots per LDS row (CPR data + 2 pad)
+  static constexpr int TILE_SLOTS = BN * SPR;
+  static constexpr int LI = (TILE_SLOTS + NT - 1) / NT;  // load instructions per wavefront per tensor per tile
+  static constexpr int TILE_BYTES = BN * RS;
   static constexpr int QSTEPS = D / M::KSTEP;
   static constexpr int DB = D / 32;
-  static_assert(TILE_CHUNKS % 64 == 0, "whole load instructions");
+  static_assert(TILE_SLOTS % 64 == 0, "whole load instructions");
 
   __device__ __forceinline__ explicit Walk(const KGeom& geom) : g(geom) {}
 
@@ -187,64 +192,248 @@ struct Walk {
   }
 
   // All wavefronts stream one tile (K and V) into a stage buffer.
-  // This lane's chunk of every load instruction: its key row inside the tile
-  // and its byte offset from the tile's first row (swizzle applied).
+  // Load instruction i of a wavefront fills 64 consecutive 16-byte LDS slots
+  // (lane l the l-th); this lane's slot holds chunk c of key row `row`, so its
+  // source is `row` and the byte offset row*D*ES + c*16 from the tile's first
+  // key.
   int drow[LI];
   uint32_t doff[LI];
   __device__ __forceinline__ void init_loads() {
 #pragma unroll
     for (int i = 0; i < LI; ++i) {
-      const int L = (i * NW + wv) * 64 + lane;
-      const int row = L / CPR, pc = L - row * CPR;
+      const int slot = (i * NW + wv) * 64 + lane;
+      const int row = min(slot / SPR, BN - 1);
+      int c = slot - (slot / SPR) * SPR;
+      c = c < CPR ? c : c - CPR;  // a pad slot re-reads a chunk its row already loads (same cache line)
       drow[i] = row;
-      doff[i] = (uint32_t)((row * D + (pc ^ (row & SWM)) * EPC) * ES);
+      doff[i] = (uint32_t)(row * D * ES + c * 16);
     }
   }
-  // Rows past `count` re-read row count-1. The base is uniform and the lane
-  // offset 32-bit, so each load is one scalar-base DMA instruction.
-  __device__ __forceinline__ void issue(char* kd, char* vd, int64_t off, int count) {
-    const char* kb = uniform_ptr(reinterpret_cast<const char*>(kc + off));
-    const char* vb = uniform_ptr(reinterpret_cast<const char*>(vc + off));
+
+  // The next tile's loads, described at the top of an iteration and issued
+  // from inside the current tile's math so the memory pipeline sees a steady
+  // trickle instead of a burst. Rows past `count` re-read row count-1. The
+  // base is uniform and the lane offset 32-bit, so each load is one
+  // scalar-base DMA instruction.
+  struct Next {
+    const char* kb;
+    const char* vb;
+    char* kd;
+    char* vd;
+    uint32_t o[LI];
+  };
+  // When the walk has no next tile the caller passes the last one again: it
+  // is re-read into the idle buffer, which nothing reads any more (cheaper
+  // than a branch around every load).
+  __device__ __forceinline__ Next next_tile(char* kd, char* vd, int64_t off, int count) const {
+    Next n;
+    n.kb = uniform_ptr(reinterpret_cast<const char*>(kc + off));
+    n.vb = uniform_ptr(reinterpret_cast<const char*>(vc + off));
+    n.kd = kd;
+    n.vd = vd;
+#pragma unroll
+    for (int i = 0; i < LI; ++i)
+      n.o[i] = count == BN ? doff[i] : doff[i] - (uint32_t)((drow[i] - min(drow[i], count - 1)) * D * ES);
+    return n;
+  }
+  // Load instruction i (of LI) of the K (V == false) or V tile.
+  // (Called with i a constant of an unrolled loop.)
+  template <bool V>
+  __device__ __forceinline__ void issue_one(const Next& n, int i) const {
+    if (i < LI) {
+      const int L0 = (i * NW + wv) * 64;
+      if ((i + 1) * NT <= TILE_SLOTS || L0 < TILE_SLOTS)
+        __builtin_amdgcn_global_load_lds((V ? n.vb : n.kb) + n.o[i], LDS_PTR(void, (V ? n.vd : n.kd) + L0 * 16), 16,
+                                         0, 0);
+    }
+  }
+  __device__ __forceinline__ void issue(const Next& n) const {
 #pragma unroll
     for (int i = 0; i < LI; ++i) {
       const int L0 = (i * NW + wv) * 64;
-      if (TILE_CHUNKS % NT == 0 || L0 < TILE_CHUNKS) {
-        const uint32_t o = count == BN ? doff[i] : doff[i] - (uint32_t)((drow[i] - min(drow[i], count - 1)) * D * ES);
-        __builtin_amdgcn_global_load_lds(kb + o, LDS_PTR(void, kd + L0 * 16), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + o, LDS_PTR(void, vd + L0 * 16), 16, 0, 0);
+      if ((i + 1) * NT <= TILE_SLOTS || L0 < TILE_SLOTS) {
+        __builtin_amdgcn_global_load_lds(n.kb + n.o[i], LDS_PTR(void, n.kd + L0 * 16), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(n.vb + n.o[i], LDS_PTR(void, n.vd + L0 * 16), 16, 0, 0);
       }
     }
   }
 
+  // ---- bf16 tile math ----------------------------------------------------
+  // K fragments of key half kh (keys 32kh .. 32kh+31) for S^T = K Q^T.
+  __device__ __forceinline__ void load_k(const char* ks, int kh, frag (&kf)[QSTEPS]) const {
+    const char* krow = ks + (kh * 32 + l32) * RS + h * 16;
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(krow + t * 32);
+  }
+  // V^T fragments (A operand) of the 16-key step ps for every 32-column block.
+  __device__ __forceinline__ void load_v(const char* vs, int ps, bf16x8 (&a)[DB]) const {
+    const int s16 = lane & 15;
+    // lane's key inside an 8-key group and its first column inside a 32-column block
+    const char* vbase = vs + (4 * h + (s16 >> 2)) * RS + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      i16x4 part[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vbase + (16 * ps + 8 * j) * RS + 64 * db));
+      a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+  __device__ __forceinline__ void mask_half(f32x16& s, int kh, int count) const {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (kh * 32 + acc_row(r, h) >= count) s[r] = -INFINITY;
+  }
+  __device__ __forceinline__ void to_bf16(const f32x16& p, bf16x8& b0, bf16x8& b1) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      b0[e] = (__bf16)p[e];
+      b1[e] = (__bf16)p[8 + e];
+    }
+  }
+  // The exact path for one half, taken when the fast path's probabilities
+  // could be too large (or the walk has no reference yet): recompute the
+  // half's scores, move the reference to the true running max (both lanes of
+  // a query row agree on it), rescale O and l, and redo the exponentials.
+  // Returns this lane's sum of the half's probabilities.
+  __device__ __forceinline__ float exact_half(const char* ks, int kh, int count, f32x16& s) {
+    frag kf[QSTEPS];
+    load_k(ks, kh, kf);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) s = M::mfma(kf[t], qf[t], s);
+    if (count < (kh + 1) * 32) mask_half(s, kh, count);
+    float mt = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+    l_run *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    const float mc = m_run * c2;
+    float ps = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
+      ps += s[r];
+    }
+    return ps;
+  }
+
+  // One bf16 tile. Online softmax without a per-tile max: probabilities are
+  // taken against the running reference m_run as they are, and only if some
+  // lane's sum of a half exceeds 2^16 (or is not finite: no reference yet)
+  // does the exact path run. Softmax is invariant to the reference, so this
+  // is exact in real arithmetic; values stay far from float32 overflow.
+  // Four groups, fenced so the MFMAs of one stage run while the exponentials
+  // of the previous one are computed: S0 | S1 + softmax(S0) | PV0 +
+  // softmax(S1) | PV1. The next tile's loads ride along in the first two.
+  static constexpr float kFastLimit = 65536.0f;
+  __device__ __forceinline__ void compute_bf16(const char* ks, const char* vs, int count, const Next& nx) {
+#define LF_FENCE __builtin_amdgcn_sched_barrier(0)
+    frag kf[QSTEPS];
+    f32x16 s0, s1;
+    load_k(ks, 0, kf);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) {
+      s0 = M::mfma(kf[t], qf[t], s0);
+      if (t & 1) issue_one<false>(nx, t / 2);
+    }
+#pragma unroll
+    for (int i = QSTEPS / 2; i < LI; ++i) issue_one<false>(nx, i);
+    LF_FENCE;
+    load_k(ks, 1, kf);
+    if (count < 32) mask_half(s0, 0, count);
+    LF_FENCE;
+    float mc = m_run * c2;
+    float ps0 = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s1[r] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) {
+      s1 = M::mfma(kf[t], qf[t], s1);
+      LF_FENCE;
+#pragma unroll
+      for (int u = 0; u < 16 / QSTEPS; ++u) {
+        const int r = t * (16 / QSTEPS) + u;
+        s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -mc));
+        ps0 += s0[r];
+      }
+      if (t & 1) issue_one<true>(nx, t / 2);
+      LF_FENCE;
+    }
+#pragma unroll
+    for (int i = QSTEPS / 2; i < LI; ++i) issue_one<true>(nx, i);
+    if (__builtin_amdgcn_ballot_w64(!(ps0 <= kFastLimit)) != 0) ps0 = exact_half(ks, 0, count, s0);
+    l_run += ps0;
+    bf16x8 b0, b1;
+    to_bf16(s0, b0, b1);
+    LF_FENCE;
+    if (count < BN) mask_half(s1, 1, count);
+    mc = m_run * c2;
+    float ps1 = 0.0f;
+    bf16x8 va[DB];
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      load_v(vs, ps, va);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        o[db] = M::mfma(va[db], ps == 0 ? b0 : b1, o[db]);
+        LF_FENCE;
+#pragma unroll
+        for (int u = 0; u < 16 / (2 * DB); ++u) {
+          const int r = (ps * DB + db) * (16 / (2 * DB)) + u;
+          s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c2, -mc));
+          ps1 += s1[r];
+        }
+        LF_FENCE;
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(!(ps1 <= kFastLimit)) != 0) ps1 = exact_half(ks, 1, count, s1);
+    l_run += ps1;
+    to_bf16(s1, b0, b1);
+    LF_FENCE;
+#pragma unroll
+    for (int ps = 2; ps < 4; ++ps) {
+      load_v(vs, ps, va);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = M::mfma(va[db], ps == 2 ? b0 : b1, o[db]);
+    }
+#undef LF_FENCE
+  }
+
+  __device__ __forceinline__ void compute(const char* ks, const char* vs, int count, const Next& nx) {
+    if constexpr (ES == 2) {
+      compute_bf16(ks, vs, count, nx);
+    } else {
+      issue(nx);
+      compute_f32(ks, vs, count);
+    }
+  }
+
+  // ---- fp32 tile math (small, correctness-oriented shapes) ----------------
   // One tile on the stage (ks, vs): S^T, online softmax, O^T += V^T P^T.
-  __device__ __forceinline__ void compute(const char* ks, const char* vs, int count) {
+  __device__ __forceinline__ void compute_f32(const char* ks, const char* vs, int count) {
     f32x16 s[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const int row = kh * 32 + l32;
-      const char* krow = ks + row * CPR * 16;
-      frag kf[QSTEPS];
-#pragma unroll
-      for (int t = 0; t < QSTEPS; ++t) {
-        if constexpr (ES == 2) {
-          const int c = 2 * t + h;
-          kf[t] = *reinterpret_cast<const bf16x8*>(krow + ((c ^ (row & SWM)) * 16));
-        } else {
-          const int d = 2 * t + h, c = d >> 2;
-          kf[t] = *reinterpret_cast<const float*>(krow + ((c ^ (row & SWM)) * 16) + 4 * (d & 3));
-        }
-      }
+      const char* krow = ks + (kh * 32 + l32) * RS + h * 4;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kh][r] = 0.0f;
 #pragma unroll
-      for (int t = 0; t < QSTEPS; ++t) s[kh] = M::mfma(kf[t], qf[t], s[kh]);
+      for (int t = 0; t < QSTEPS; ++t) s[kh] = M::mfma(*reinterpret_cast<const frag*>(krow + t * 8), qf[t], s[kh]);
     }
     if (count < BN) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kh * 32 + acc_row(r, h) >= count) s[kh][r] = -INFINITY;
+      for (int kh = 0; kh < 2; ++kh) mask_half(s[kh], kh, count);
     }
     float mt = -INFINITY;
 #pragma unroll
@@ -252,19 +441,14 @@ struct Walk {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kh][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // Lazy rescale: the reference max moves (and O, l are rescaled) only when
-    // some row's max grew by more than 8 in log2 units; otherwise the stale
-    // max stays, every p <= 2^8, and the softmax is unchanged in exact math.
     const float m_new = fmaxf(m_run, mt);
-    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c2 > 8.0f) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-      l_run *= alpha;
-      m_run = m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+    l_run *= alpha;
+    m_run = m_new;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     const float mc = m_run * c2;
     float psum = 0.0f;
 #pragma unroll
@@ -276,46 +460,12 @@ struct Walk {
         psum += p;
       }
     l_run += psum;
-
-    if constexpr (ES == 2) {
-      const int grp = lane >> 4, s16 = lane & 15;
 #pragma unroll
-      for (int ps = 0; ps < BN / 16; ++ps) {
-        bf16x8 b;
-        const int kh = ps >> 1, r0 = (ps & 1) * 8;
+    for (int ps = 0; ps < BN / 2; ++ps) {
+      const int kh = ps >> 4, r = ps & 15;
+      const char* vrow = vs + (kh * 32 + acc_row(r, h)) * RS + l32 * 4;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) b[e] = (__bf16)s[kh][r0 + e];
-        bf16x8 a[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int col = 32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
-          const int c = col >> 3, byte = (col & 7) * 2;
-          i16x4 part[2];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int key = 16 * ps + 8 * j + 4 * h + (s16 >> 2);
-            part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                LDS_PTR(i16x4, vs + (key * CPR + (c ^ (key & SWM))) * 16 + byte));
-          }
-          a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = M::mfma(a[db], b, o[db]);
-      }
-    } else {
-#pragma unroll
-      for (int ps = 0; ps < BN / 2; ++ps) {
-        const int kh = ps >> 4, r = ps & 15;
-        const float b = s[kh][r];
-        const int key = kh * 32 + acc_row(r, h);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int dcol = 32 * db + l32;
-          const float a = *reinterpret_cast<const float*>(vs + (key * CPR + ((dcol >> 2) ^ (key & SWM))) * 16 +
-                                                          4 * (dcol & 3));
-          o[db] = M::mfma(a, b, o[db]);
-        }
-      }
+      for (int db = 0; db < DB; ++db) o[db] = M::mfma(*reinterpret_cast<const frag*>(vrow + db * 128), s[kh][r], o[db]);
     }
   }
 };
@@ -413,15 +563,18 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), WG_PER_CU<T>) void attn_kerne
   int64_t noff = 0;
   int ncount = 0, nmask = 0;
   bool have = w.produce(noff, ncount, nmask);
-  if (have) w.issue(k0, v0, noff, ncount);
+  if (have) w.issue(w.next_tile(k0, v0, noff, ncount));
   while (have) {
     {
       const int count = ncount, mask = nmask;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wavefront's share of the tile has landed
       __syncthreads();                       // ... everyone's, and the other buffer is free
       have = w.produce(noff, ncount, nmask);
-      if (have) w.issue(k1, v1, noff, ncount);
-      if (w.wave_active && ((mask >> w.lq) & 1)) w.compute(k0, v0, count);
+      const typename W::Next nx = w.next_tile(k1, v1, noff, ncount);
+      if (w.wave_active && ((mask >> w.lq) & 1))
+        w.compute(k0, v0, count, nx);
+      else
+        w.issue(nx);
     }
     if (!have) break;
     {
@@ -429,11 +582,16 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), WG_PER_CU<T>) void attn_kerne
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       have = w.produce(noff, ncount, nmask);
-      if (have) w.issue(k0, v0, noff, ncount);
-      if (w.wave_active && ((mask >> w.lq) & 1)) w.compute(k1, v1, count);
+      const typename W::Next nx = w.next_tile(k0, v0, noff, ncount);
+      if (w.wave_active && ((mask >> w.lq) & 1))
+        w.compute(k1, v1, count, nx);
+      else
+        w.issue(nx);
     }
   }
 
+  // No load may still be writing LDS when the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   if (!w.wave_active || w.qr >= w.nrows) return;
   const float l_tot = w.l_run + __shfl_xor(w.l_run, 32);
   const float inv = 1.0f / l_tot;
