@@ -82,6 +82,15 @@ __device__ inline P* uniform_ptr(P* p) {
 // output (rows = keys): 8*(r/4) + 4*h + r%4.
 __device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Pins a computed value at this point of the program: an empty asm that
+// claims to modify the register, so no optimisation pass moves the
+// computation past it (the scheduling fences alone bind only the final
+// instruction scheduler). Emits no instruction.
+__device__ inline float pin(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Workgroups per CU to plan registers for: two for bf16 (their wavefronts
 // pair up on each SIMD, so one's softmax hides under the other's MFMAs);
 // fp32 inputs (small, correctness-oriented shapes) get the register file.
@@ -265,19 +274,23 @@ struct Walk {
 #pragma unroll
     for (int t = 0; t < QSTEPS; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(krow + t * 32);
   }
+  __device__ __forceinline__ frag load_k1(const char* ks, int kh, int t) const {
+    return *reinterpret_cast<const bf16x8*>(ks + (kh * 32 + l32) * RS + h * 16 + t * 32);
+  }
   // V^T fragments (A operand) of the 16-key step ps for every 32-column block.
   __device__ __forceinline__ void load_v(const char* vs, int ps, bf16x8 (&a)[DB]) const {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) a[db] = load_v1(vs, ps, db);
+  }
+  __device__ __forceinline__ bf16x8 load_v1(const char* vs, int ps, int db) const {
     const int s16 = lane & 15;
     // lane's key inside an 8-key group and its first column inside a 32-column block
     const char* vbase = vs + (4 * h + (s16 >> 2)) * RS + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+    i16x4 part[2];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      i16x4 part[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vbase + (16 * ps + 8 * j) * RS + 64 * db));
-      a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+    for (int j = 0; j < 2; ++j)
+      part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vbase + (16 * ps + 8 * j) * RS + 64 * db));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
   }
   __device__ __forceinline__ void mask_half(f32x16& s, int kh, int count) const {
 #pragma unroll
@@ -297,12 +310,16 @@ struct Walk {
   // a query row agree on it), rescale O and l, and redo the exponentials.
   // Returns this lane's sum of the half's probabilities.
   __device__ __forceinline__ float exact_half(const char* ks, int kh, int count, f32x16& s) {
-    frag kf[QSTEPS];
-    load_k(ks, kh, kf);
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+    // one fragment at a time (fenced): this path is rare and must not raise
+    // the register high-water mark of the kernel
 #pragma unroll
-    for (int t = 0; t < QSTEPS; ++t) s = M::mfma(kf[t], qf[t], s);
+    for (int t = 0; t < QSTEPS; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      s = M::mfma(load_k1(ks, kh, t), qf[t], s);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (count < (kh + 1) * 32) mask_half(s, kh, count);
     float mt = s[0];
 #pragma unroll
@@ -338,21 +355,28 @@ struct Walk {
   __device__ __forceinline__ void compute_bf16(const char* ks, const char* vs, int count, const Next& nx) {
 #define LF_FENCE __builtin_amdgcn_sched_barrier(0)
     frag kf[QSTEPS];
+    bf16x8 va[DB];
     f32x16 s0, s1;
+    // A: S0 = K[0:32] Q^T; each K fragment register is refilled with the
+    // matching K[32:64] fragment as soon as its MFMA has been issued, and the
+    // next K tile's DMA goes out.
     load_k(ks, 0, kf);
+    LF_FENCE;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s0[r] = 0.0f;
 #pragma unroll
     for (int t = 0; t < QSTEPS; ++t) {
       s0 = M::mfma(kf[t], qf[t], s0);
+      kf[t] = load_k1(ks, 1, t);
       if (t & 1) issue_one<false>(nx, t / 2);
+      LF_FENCE;
     }
 #pragma unroll
     for (int i = QSTEPS / 2; i < LI; ++i) issue_one<false>(nx, i);
-    LF_FENCE;
-    load_k(ks, 1, kf);
     if (count < 32) mask_half(s0, 0, count);
     LF_FENCE;
+    // B: S1 = K[32:64] Q^T with the softmax of S0 between its MFMAs; the
+    // first V fragments are read and the next V tile's DMA goes out.
     float mc = m_run * c2;
     float ps0 = 0.0f;
 #pragma unroll
@@ -364,9 +388,10 @@ struct Walk {
 #pragma unroll
       for (int u = 0; u < 16 / QSTEPS; ++u) {
         const int r = t * (16 / QSTEPS) + u;
-        s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -mc));
+        s0[r] = pin(__builtin_amdgcn_exp2f(fmaf(s0[r], c2, -mc)));
         ps0 += s0[r];
       }
+      if (t >= QSTEPS - DB) va[t - (QSTEPS - DB)] = load_v1(vs, 0, t - (QSTEPS - DB));
       if (t & 1) issue_one<true>(nx, t / 2);
       LF_FENCE;
     }
@@ -376,36 +401,38 @@ struct Walk {
     l_run += ps0;
     bf16x8 b0, b1;
     to_bf16(s0, b0, b1);
-    LF_FENCE;
     if (count < BN) mask_half(s1, 1, count);
+    LF_FENCE;
+    // C: O^T += V[0:32]^T P0^T with the softmax of S1 between its MFMAs. V
+    // fragments roll: after the MFMA of 16-key step ps, column block db, the
+    // register is refilled with step ps+1's fragment of the same block.
     mc = m_run * c2;
     float ps1 = 0.0f;
-    bf16x8 va[DB];
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      load_v(vs, ps, va);
+    for (int j = 0; j < 2 * DB; ++j) {
+      const int ps = j / DB, db = j % DB;
+      o[db] = M::mfma(va[db], ps == 0 ? b0 : b1, o[db]);
+      va[db] = load_v1(vs, ps + 1, db);
+      LF_FENCE;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        o[db] = M::mfma(va[db], ps == 0 ? b0 : b1, o[db]);
-        LF_FENCE;
-#pragma unroll
-        for (int u = 0; u < 16 / (2 * DB); ++u) {
-          const int r = (ps * DB + db) * (16 / (2 * DB)) + u;
-          s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c2, -mc));
-          ps1 += s1[r];
-        }
-        LF_FENCE;
+      for (int u = 0; u < 16 / (2 * DB); ++u) {
+        const int r = j * (16 / (2 * DB)) + u;
+        s1[r] = pin(__builtin_amdgcn_exp2f(fmaf(s1[r], c2, -mc)));
+        ps1 += s1[r];
       }
+      LF_FENCE;
     }
     if (__builtin_amdgcn_ballot_w64(!(ps1 <= kFastLimit)) != 0) ps1 = exact_half(ks, 1, count, s1);
     l_run += ps1;
     to_bf16(s1, b0, b1);
     LF_FENCE;
+    // D: O^T += V[32:64]^T P1^T.
 #pragma unroll
-    for (int ps = 2; ps < 4; ++ps) {
-      load_v(vs, ps, va);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = M::mfma(va[db], ps == 2 ? b0 : b1, o[db]);
+    for (int j = 0; j < 2 * DB; ++j) {
+      const int ps = 2 + j / DB, db = j % DB;
+      o[db] = M::mfma(va[db], ps == 2 ? b0 : b1, o[db]);
+      if (ps == 2) va[db] = load_v1(vs, 3, db);
+      LF_FENCE;
     }
 #undef LF_FENCE
   }
