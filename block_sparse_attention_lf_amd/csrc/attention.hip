@@ -140,63 +140,34 @@ struct Walk {
   f32x16 o[DB];
   float m_run, l_run, c2;
   // producer state (uniform)
-  const int32_t* lists;  // LDS copy, QPW rows of LF_MAX_SEL
-  int len[QPW], pos[QPW];
-  int tpf, n_cur, n_hist_blocks, all_mask, cur_next, hb_start, hb_end, hb_mask;
-  int64_t frame_elems, bh_base, hb_base;
+  const uint32_t* walk;  // LDS table of history tiles, see the kernel
+  int tpf, n_cur, n_tiles, all_mask, t_next, cf, ct;
+  int64_t frame_elems, bh_base, cur_base;
 
-  // Next block of the merged ascending union of the lists (ids outside
-  // [0, Fh*nb) are skipped); false when every list is exhausted. Updates are
-  // branch-free so the list state stays in scalar registers.
-  __device__ __forceinline__ bool next_block(int& id_out, int& mask_out) {
-    for (;;) {
-      int id = INT32_MAX;
-      int hd[QPW];
-#pragma unroll
-      for (int i = 0; i < QPW; ++i) {
-        const int v = __builtin_amdgcn_readfirstlane(lists[i * LF_MAX_SEL + min(pos[i], LF_MAX_SEL - 1)]);
-        hd[i] = pos[i] < len[i] ? v : INT32_MAX;
-        id = min(id, hd[i]);
-      }
-      if (id == INT32_MAX) return false;
-      int mask = 0;
-#pragma unroll
-      for (int i = 0; i < QPW; ++i) {
-        const int hit = hd[i] == id;
-        mask |= hit << i;
-        pos[i] += hit;
-      }
-      if (id >= 0 && id < n_hist_blocks) {
-        id_out = id;
-        mask_out = mask;
-        return true;
-      }
-    }
-  }
-
-  // Fills (off, count, mask) of the next tile: the current chunk's tiles,
-  // then the union's history blocks (tiles of up to BN keys inside each);
-  // false when the walk is over. The counters advance with selects, not in
-  // separate branches, so that the compiler keeps them in registers.
+  // Fills (off, count, mask) of the next tile: the current chunk's tiles in
+  // order (counters, no divisions), then the history tiles of the table;
+  // false when the walk is over.
   __device__ __forceinline__ bool produce(int64_t& off, int& count, int& mask) {
-    const bool is_cur = cur_next < n_cur;
-    if (!is_cur && hb_start >= hb_end) {
-      int id, m;
-      if (!next_block(id, m)) return false;
-      const int f = id / g.nb, j = id - f * g.nb;
-      hb_mask = m;
-      hb_start = j * g.b;
-      hb_end = min(hb_start + g.b, g.T);
-      hb_base = bh_base + g.slot[f] * frame_elems;
+    if (t_next >= n_tiles) return false;
+    if (t_next < n_cur) {
+      const int start = ct * BN;
+      off = cur_base + (int64_t)start * D;
+      count = min(BN, g.T - start);
+      mask = all_mask;
+      if (++ct == tpf) {
+        ct = 0;
+        ++cf;
+        cur_base = bh_base + (int64_t)g.slot[g.Fh + min(cf, g.Fc - 1)] * frame_elems;
+      }
+    } else {
+      const uint32_t e = __builtin_amdgcn_readfirstlane(walk[t_next - n_cur]);
+      const int f = (int)(e >> 14), j = (int)((e >> 5) & 511), sub = (int)((e >> 4) & 1);
+      const int start = j * g.b + sub * BN;
+      off = bh_base + (int64_t)g.slot[f] * frame_elems + (int64_t)start * D;
+      count = min(BN, min(j * g.b + g.b, g.T) - start);
+      mask = (int)(e & 15);
     }
-    const int cf = min(cur_next, n_cur - 1) / tpf;
-    const int c_start = (min(cur_next, n_cur - 1) - cf * tpf) * BN;
-    const int64_t c_off = bh_base + g.slot[g.Fh + cf] * frame_elems + (int64_t)c_start * D;
-    off = is_cur ? c_off : hb_base + (int64_t)hb_start * D;
-    count = is_cur ? min(BN, g.T - c_start) : min(BN, hb_end - hb_start);
-    mask = is_cur ? all_mask : hb_mask;
-    cur_next += is_cur ? 1 : 0;
-    hb_start += is_cur ? 0 : BN;
+    ++t_next;
     return true;
   }
 
@@ -503,7 +474,7 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), WG_PER_CU<T>) void attn_kerne
     const int32_t* __restrict__ nsel, int max_sel, float scale, const KGeom g, T* __restrict__ out,
     float* __restrict__ lse) {
   using W = Walk<T, D, WPQ>;
-  constexpr int QPW = W::QPW, NT = W::NT, ES = W::ES, QSTEPS = W::QSTEPS, DB = W::DB;
+  constexpr int QPW = W::QPW, ES = W::ES, QSTEPS = W::QSTEPS, DB = W::DB;
 
   // Two named stage buffers (not one indexed array): the loop below is
   // unrolled by two so every LDS read names its buffer at compile time, which
@@ -513,8 +484,10 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), WG_PER_CU<T>) void attn_kerne
   __shared__ __attribute__((aligned(1024))) char v0[W::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1[W::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v1[W::TILE_BYTES];
-  // The selected-block lists of this workgroup's query blocks, copied once.
-  __shared__ int32_t lists[QPW * LF_MAX_SEL];
+  // History tiles of the walk, one packed entry each (see below); a block of
+  // more than BN keys is two tiles.
+  constexpr int WALK_CAP = QPW * LF_MAX_SEL * (WPQ > 2 ? 2 : 1);
+  __shared__ uint32_t walk[WALK_CAP];
 
   W w(g);
   w.kc = kc;
@@ -559,24 +532,97 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), WG_PER_CU<T>) void attn_kerne
   // Producer state.
   w.tpf = (g.T + BN - 1) / BN;
   w.n_cur = g.Fc * w.tpf;
-  w.n_hist_blocks = g.Fh * g.nb;
   w.frame_elems = (int64_t)g.T * D;
   w.bh_base = w.bh * g.S * w.frame_elems;
   w.all_mask = (1 << min(QPW, g.nqb - w.qb0)) - 1;
-  w.lists = lists;
+  w.t_next = 0;
+  w.cf = 0;
+  w.ct = 0;
+  w.cur_base = w.bh_base + (int64_t)g.slot[g.Fh] * w.frame_elems;
+  w.walk = walk;
+
+  // History walk table. Each query block's selected ids are first compacted
+  // (ids outside [0, Fh*nb) dropped) into the still unused first K buffer,
+  // one wavefront per list. Then every wavefront computes the same table
+  // positions (wavefront 0 writes): the blocks of list 0, then those of
+  // list 1 that list 0 lacks, and so on, each with the mask of all query
+  // blocks that selected it, so a shared block is loaded once. Membership is
+  // a binary search, valid when every list ascends; if one does not, no
+  // block is shared (each list walks its own blocks with only its own bit),
+  // which is still exact. Entry: frame << 14 | block << 5 | sub-tile << 4 | mask.
+  {
+    int32_t* stage = reinterpret_cast<int32_t*>(k0);
+    int32_t* stage_len = stage + QPW * LF_MAX_SEL;
+    static_assert((QPW * LF_MAX_SEL + QPW) * 4 <= W::TILE_BYTES, "lists must fit in one K buffer");
+    const int n_hist_blocks = g.Fh * g.nb;
+    const uint64_t lt = (1ull << w.lane) - 1;  // lanes below this one
+    if (w.wv < QPW) {
+      const int i = w.wv, qbi = w.qb0 + i;
+      const int64_t row = w.bh * g.nqb + qbi;
+      const int len = (qbi < g.nqb && max_sel > 0) ? __builtin_amdgcn_readfirstlane(min(max(nsel[row], 0), max_sel)) : 0;
+      int n = 0;
+      for (int j0 = 0; j0 < len; j0 += 64) {
+        const int j = j0 + w.lane;
+        const int x = j < len ? sel[row * max_sel + j] : -1;
+        const bool valid = x >= 0 && x < n_hist_blocks;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(valid);
+        if (valid) stage[i * LF_MAX_SEL + n + __builtin_popcountll(bal & lt)] = x;
+        n += __builtin_popcountll(bal);
+      }
+      if (w.lane == 0) stage_len[i] = n;
+    }
+    __syncthreads();
+    int clen[QPW];
 #pragma unroll
-  for (int i = 0; i < QPW; ++i) {
-    const int qbi = w.qb0 + i;
-    const int64_t row = w.bh * g.nqb + qbi;
-    w.len[i] = (qbi < g.nqb && max_sel > 0) ? __builtin_amdgcn_readfirstlane(min(max(nsel[row], 0), max_sel)) : 0;
-    w.pos[i] = 0;
-    for (int j = tid; j < w.len[i]; j += NT) lists[i * LF_MAX_SEL + j] = sel[row * max_sel + j];
+    for (int i = 0; i < QPW; ++i) clen[i] = __builtin_amdgcn_readfirstlane(stage_len[i]);
+    bool sorted = true;
+#pragma unroll
+    for (int i = 0; i < QPW; ++i)
+      for (int k0s = 0; k0s < clen[i]; k0s += 64) {
+        const int k = k0s + w.lane;
+        const bool bad = k + 1 < clen[i] && stage[i * LF_MAX_SEL + k] >= stage[i * LF_MAX_SEL + k + 1];
+        sorted = sorted && __builtin_amdgcn_ballot_w64(bad) == 0;
+      }
+    int n_hist_tiles = 0;
+#pragma unroll
+    for (int i = 0; i < QPW; ++i)
+      for (int k0s = 0; k0s < clen[i]; k0s += 64) {
+        const int k = k0s + w.lane;
+        const bool valid = k < clen[i];
+        const int x = valid ? stage[i * LF_MAX_SEL + k] : 0;
+        int mask = 1 << i;
+        bool owned = valid;
+        if (sorted && QPW > 1) {
+#pragma unroll
+          for (int i2 = 0; i2 < QPW; ++i2) {
+            if (i2 == i) continue;
+            const int32_t* l2 = stage + i2 * LF_MAX_SEL;
+            int lo = 0, hi = clen[i2];
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if (l2[mid] < x) lo = mid + 1; else hi = mid;
+            }
+            if (lo < clen[i2] && l2[lo] == x) {
+              mask |= 1 << i2;
+              if (i2 < i) owned = false;
+            }
+          }
+        }
+        const int f = x / g.nb, j = x - f * g.nb;
+        const bool two = min(g.b, g.T - j * g.b) > BN;
+        const uint64_t b1 = __builtin_amdgcn_ballot_w64(owned), b2 = __builtin_amdgcn_ballot_w64(owned && two);
+        const int pos = n_hist_tiles + __builtin_popcountll(b1 & lt) + __builtin_popcountll(b2 & lt);
+        if (w.wv == 0 && owned) {
+          const uint32_t e = ((uint32_t)f << 14) | ((uint32_t)j << 5) | (uint32_t)mask;
+          walk[pos] = e;
+          if (two) walk[pos + 1] = e | (1u << 4);
+        }
+        n_hist_tiles += __builtin_popcountll(b1) + __builtin_popcountll(b2);
+      }
+    w.n_tiles = w.n_cur + n_hist_tiles;
+    __syncthreads();  // the table is written and the first K buffer is free again
   }
-  __syncthreads();
-  w.cur_next = 0;
   w.init_loads();
-  w.hb_start = w.hb_end = w.hb_mask = 0;
-  w.hb_base = 0;
 
 #pragma unroll
   for (int db = 0; db < DB; ++db)
