@@ -92,10 +92,12 @@ __device__ inline float pin(float x) {
 }
 
 // Workgroups per CU to plan registers for: two for bf16 (their wavefronts
-// pair up on each SIMD, so one's softmax hides under the other's MFMAs);
-// fp32 inputs (small, correctness-oriented shapes) get the register file.
-template <typename T>
-constexpr int WG_PER_CU = sizeof(T) == 2 ? 2 : 1;
+// pair up on each SIMD, so one's softmax hides under the other's MFMAs),
+// except with four query blocks per workgroup (blocks of at most 32 keys),
+// whose larger walk table leaves LDS for one; fp32 inputs (small,
+// correctness-oriented shapes) get the register file.
+template <typename T, int WPQ>
+constexpr int WG_PER_CU = sizeof(T) == 2 && WPQ > 1 ? 2 : 1;
 
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 only.
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
@@ -140,7 +142,7 @@ struct Walk {
   f32x16 o[DB];
   float m_run, l_run, c2;
   // producer state (uniform)
-  const uint32_t* walk;  // LDS table of history tiles, see the kernel
+  const uint2* walk;  // LDS table of history tiles, see the kernel
   int tpf, n_cur, n_tiles, all_mask, t_next, cf, ct;
   int64_t frame_elems, bh_base, cur_base;
 
@@ -160,12 +162,11 @@ struct Walk {
         cur_base = bh_base + (int64_t)g.slot[g.Fh + min(cf, g.Fc - 1)] * frame_elems;
       }
     } else {
-      const uint32_t e = __builtin_amdgcn_readfirstlane(walk[t_next - n_cur]);
-      const int f = (int)(e >> 14), j = (int)((e >> 5) & 511), sub = (int)((e >> 4) & 1);
-      const int start = j * g.b + sub * BN;
-      off = bh_base + (int64_t)g.slot[f] * frame_elems + (int64_t)start * D;
-      count = min(BN, min(j * g.b + g.b, g.T) - start);
-      mask = (int)(e & 15);
+      const uint2 e = walk[t_next - n_cur];
+      off = (int64_t)__builtin_amdgcn_readfirstlane(e.x) * D;
+      const int cm = __builtin_amdgcn_readfirstlane(e.y);
+      count = cm & 255;
+      mask = cm >> 8;
     }
     ++t_next;
     return true;
@@ -173,10 +174,8 @@ struct Walk {
 
   // All wavefronts stream one tile (K and V) into a stage buffer.
   // Load instruction i of a wavefront fills 64 consecutive 16-byte LDS slots
-  // (lane l the l-th); this lane's slot holds chunk c of key row `row`, so its
-  // source is `row` and the byte offset row*D*ES + c*16 from the tile's first
-  // key.
-  int drow[LI];
+  // (lane l the l-th); this lane's slot holds chunk c of key row `row`, i.e.
+  // byte offset row*D*ES + c*16 from the tile's first key.
   uint32_t doff[LI];
   __device__ __forceinline__ void init_loads() {
 #pragma unroll
@@ -185,35 +184,33 @@ struct Walk {
       const int row = min(slot / SPR, BN - 1);
       int c = slot - (slot / SPR) * SPR;
       c = c < CPR ? c : c - CPR;  // a pad slot re-reads a chunk its row already loads (same cache line)
-      drow[i] = row;
       doff[i] = (uint32_t)(row * D * ES + c * 16);
     }
   }
 
   // The next tile's loads, described at the top of an iteration and issued
   // from inside the current tile's math so the memory pipeline sees a steady
-  // trickle instead of a burst. Rows past `count` re-read row count-1. The
-  // base is uniform and the lane offset 32-bit, so each load is one
-  // scalar-base DMA instruction.
+  // trickle instead of a burst. Each tensor's tile is addressed through a
+  // buffer resource whose size is the tile's valid rows: the hardware returns
+  // zeros for rows past `count`, so a ragged tile needs no per-lane clamping
+  // and no load leaves the tile.
   struct Next {
-    const char* kb;
-    const char* vb;
+    __amdgpu_buffer_rsrc_t rk, rv;
     char* kd;
     char* vd;
-    uint32_t o[LI];
   };
+  // Buffer resource word 3 for raw (untyped) dword access on this GPU family.
+  static constexpr int kRawBufferFlags = 0x00020000;
   // When the walk has no next tile the caller passes the last one again: it
   // is re-read into the idle buffer, which nothing reads any more (cheaper
   // than a branch around every load).
   __device__ __forceinline__ Next next_tile(char* kd, char* vd, int64_t off, int count) const {
     Next n;
-    n.kb = uniform_ptr(reinterpret_cast<const char*>(kc + off));
-    n.vb = uniform_ptr(reinterpret_cast<const char*>(vc + off));
+    const int bytes = count * D * ES;
+    n.rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(uniform_ptr(kc + off)), (short)0, bytes, kRawBufferFlags);
+    n.rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(uniform_ptr(vc + off)), (short)0, bytes, kRawBufferFlags);
     n.kd = kd;
     n.vd = vd;
-#pragma unroll
-    for (int i = 0; i < LI; ++i)
-      n.o[i] = count == BN ? doff[i] : doff[i] - (uint32_t)((drow[i] - min(drow[i], count - 1)) * D * ES);
     return n;
   }
   // Load instruction i (of LI) of the K (V == false) or V tile.
@@ -222,19 +219,23 @@ struct Walk {
   __device__ __forceinline__ void issue_one(const Next& n, int i) const {
     if (i < LI) {
       const int L0 = (i * NW + wv) * 64;
+      // (the buffer-to-LDS builtin exists only for the device compilation
+      // pass; the host pass never runs this function)
+#if defined(__HIP_DEVICE_COMPILE__)
       if ((i + 1) * NT <= TILE_SLOTS || L0 < TILE_SLOTS)
-        __builtin_amdgcn_global_load_lds((V ? n.vb : n.kb) + n.o[i], LDS_PTR(void, (V ? n.vd : n.kd) + L0 * 16), 16,
-                                         0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(V ? n.rv : n.rk, LDS_PTR(void, (V ? n.vd : n.kd) + L0 * 16), 16,
+                                                 doff[i], 0, 0, 0);
+#else
+      (void)n;
+      (void)L0;
+#endif
     }
   }
   __device__ __forceinline__ void issue(const Next& n) const {
 #pragma unroll
     for (int i = 0; i < LI; ++i) {
-      const int L0 = (i * NW + wv) * 64;
-      if ((i + 1) * NT <= TILE_SLOTS || L0 < TILE_SLOTS) {
-        __builtin_amdgcn_global_load_lds(n.kb + n.o[i], LDS_PTR(void, n.kd + L0 * 16), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(n.vb + n.o[i], LDS_PTR(void, n.vd + L0 * 16), 16, 0, 0);
-      }
+      issue_one<false>(n, i);
+      issue_one<true>(n, i);
     }
   }
 
@@ -469,7 +470,7 @@ struct Walk {
 };
 
 template <typename T, int D, int WPQ>
-__global__ __launch_bounds__(64 * WPQ * (4 / WPQ), WG_PER_CU<T>) void attn_kernel(
+__global__ __launch_bounds__(64 * WPQ * (4 / WPQ), (WG_PER_CU<T, WPQ>)) void attn_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ nsel, int max_sel, float scale, const KGeom g, T* __restrict__ out,
     float* __restrict__ lse) {
@@ -484,10 +485,10 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), WG_PER_CU<T>) void attn_kerne
   __shared__ __attribute__((aligned(1024))) char v0[W::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1[W::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v1[W::TILE_BYTES];
-  // History tiles of the walk, one packed entry each (see below); a block of
-  // more than BN keys is two tiles.
+  // History tiles of the walk, one entry each (see below); a block of more
+  // than BN keys is two tiles.
   constexpr int WALK_CAP = QPW * LF_MAX_SEL * (WPQ > 2 ? 2 : 1);
-  __shared__ uint32_t walk[WALK_CAP];
+  __shared__ uint2 walk[WALK_CAP];
 
   W w(g);
   w.kc = kc;
@@ -549,7 +550,9 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), WG_PER_CU<T>) void attn_kerne
   // blocks that selected it, so a shared block is loaded once. Membership is
   // a binary search, valid when every list ascends; if one does not, no
   // block is shared (each list walks its own blocks with only its own bit),
-  // which is still exact. Entry: frame << 14 | block << 5 | sub-tile << 4 | mask.
+  // which is still exact. Entry: (cache row of the tile's first key,
+  // key count | query-block mask << 8); cache rows are counted over
+  // [B, H, S, T] and fit 32 bits (checked on the host).
   {
     int32_t* stage = reinterpret_cast<int32_t*>(k0);
     int32_t* stage_len = stage + QPW * LF_MAX_SEL;
@@ -613,9 +616,10 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), WG_PER_CU<T>) void attn_kerne
         const uint64_t b1 = __builtin_amdgcn_ballot_w64(owned), b2 = __builtin_amdgcn_ballot_w64(owned && two);
         const int pos = n_hist_tiles + __builtin_popcountll(b1 & lt) + __builtin_popcountll(b2 & lt);
         if (w.wv == 0 && owned) {
-          const uint32_t e = ((uint32_t)f << 14) | ((uint32_t)j << 5) | (uint32_t)mask;
-          walk[pos] = e;
-          if (two) walk[pos + 1] = e | (1u << 4);
+          const int start = j * g.b, end = min(start + g.b, g.T);
+          const uint32_t row = (uint32_t)((w.bh * g.S + g.slot[f]) * g.T + start);
+          walk[pos] = make_uint2(row, (uint32_t)(min(BN, end - start) | (mask << 8)));
+          if (two) walk[pos + 1] = make_uint2(row + BN, (uint32_t)(min(BN, end - start - BN) | (mask << 8)));
         }
         n_hist_tiles += __builtin_popcountll(b1) + __builtin_popcountll(b2);
       }

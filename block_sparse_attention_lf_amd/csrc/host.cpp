@@ -41,7 +41,7 @@ lf_status make_geom(const lf_geom* g, const int32_t* frame_slot, lf::KGeom* kg) 
   const int64_t lq = (int64_t)g->chunk_frames * g->tokens_per_frame;
   const int64_t bh = (int64_t)g->batch * g->heads;
   if (lq > INT32_MAX / 2 || bh * g->chunk_frames * nb > INT32_MAX / 8 ||
-      bh * g->cache_slots * (int64_t)g->tokens_per_frame > ((int64_t)1 << 40))
+      bh * g->cache_slots * (int64_t)g->tokens_per_frame >= ((int64_t)1 << 32))
     return fail(LF_ERR_GEOM, "problem too large for one call");
   kg->B = g->batch;
   kg->H = g->heads;

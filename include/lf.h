@@ -90,7 +90,7 @@ typedef struct {
   int32_t chunk_frames;     /* Fc >= 1 */
   int32_t hist_frames;      /* Fh >= 0; Fh + Fc <= LF_MAX_FRAMES */
   int32_t n_sink;           /* 0 <= n_sink <= Fh */
-  int32_t cache_slots;      /* >= Fh + Fc */
+  int32_t cache_slots;      /* >= Fh + Fc; B*H*cache_slots*T < 2^32 */
   int32_t dtype;            /* lf_dtype */
 } lf_geom;
 
