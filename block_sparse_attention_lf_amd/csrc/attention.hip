@@ -91,13 +91,15 @@ __device__ inline float pin(float x) {
   return x;
 }
 
-// Workgroups per CU to plan registers for: two for bf16 (their wavefronts
-// pair up on each SIMD, so one's softmax hides under the other's MFMAs),
-// except with four query blocks per workgroup (blocks of at most 32 keys),
-// whose larger walk table leaves LDS for one; fp32 inputs (small,
-// correctness-oriented shapes) get the register file.
+// Wavefronts per SIMD to plan registers for (the second launch bound). With
+// bf16, LDS holds two workgroups' stage buffers, i.e. two wavefronts per
+// SIMD (256 registers each), which pair up so that one's softmax hides under
+// the other's MFMAs. Blocks of at most 32 keys (four query blocks per
+// workgroup, a larger walk table) fit one workgroup per CU, and fp32 inputs
+// (small, correctness-oriented shapes) run one wavefront per SIMD with the
+// whole register file.
 template <typename T, int WPQ>
-constexpr int WG_PER_CU = sizeof(T) == 2 && WPQ > 1 ? 2 : 1;
+constexpr int WAVES_PER_SIMD = sizeof(T) == 2 && WPQ > 1 ? 2 : 1;
 
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 only.
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
@@ -470,7 +472,7 @@ struct Walk {
 };
 
 template <typename T, int D, int WPQ>
-__global__ __launch_bounds__(64 * WPQ * (4 / WPQ), (WG_PER_CU<T, WPQ>)) void attn_kernel(
+__global__ __launch_bounds__(64 * WPQ * (4 / WPQ), (WAVES_PER_SIMD<T, WPQ>)) void attn_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ nsel, int max_sel, float scale, const KGeom g, T* __restrict__ out,
     float* __restrict__ lse) {
