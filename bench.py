@@ -188,7 +188,7 @@ def main():
         sl = host_side()
         if ev is not None:
             ev[0].record(stream)
-        lf.lf_compress(g, q, kc, sl, bufs.q_blk, bufs.k_blk, bufs.k_frm, bufs.workspace, stream)
+        lf.lf_compress(g, q, kc, sl, bufs.q_blk, bufs.k_blk, bufs.k_frm, stream)
         if ev is not None:
             ev[1].record(stream)
         lf.lf_select(g, bufs.q_blk, bufs.k_blk, bufs.k_frm, w.k_frames, w.k_blocks, bufs.sel_frames,

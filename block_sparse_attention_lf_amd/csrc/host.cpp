@@ -88,7 +88,6 @@ const char* lf_status_str(lf_status s) {
     case LF_ERR_K: return "LF_ERR_K";
     case LF_ERR_ALIGN: return "LF_ERR_ALIGN";
     case LF_ERR_HIP: return "LF_ERR_HIP";
-    case LF_ERR_WORKSPACE: return "LF_ERR_WORKSPACE";
     case LF_ERR_SLOT: return "LF_ERR_SLOT";
     case LF_ERR_ARG: return "LF_ERR_ARG";
   }
@@ -97,29 +96,19 @@ const char* lf_status_str(lf_status s) {
 
 const char* lf_last_error(void) { return g_err; }
 
-size_t lf_compress_workspace_bytes(const lf_geom* g) {
-  lf::KGeom kg;
-  if (make_geom(g, nullptr, &kg) != LF_OK) return 0;
-  return (size_t)kg.B * kg.H * kg.Fh * kg.nb * kg.D * sizeof(double);
-}
-
 lf_status lf_compress(const lf_geom* g, const void* q, const void* k_cache, const int32_t* frame_slot, float* q_blk,
-                      float* k_blk, float* k_frm, void* workspace, size_t workspace_bytes, lf_stream stream) {
+                      float* k_blk, float* k_frm, lf_stream stream) {
   if (frame_slot == nullptr) return fail(LF_ERR_NULL, "frame_slot is NULL");
   lf::KGeom kg;
   lf_status st = make_geom(g, frame_slot, &kg);
   if (st != LF_OK) return st;
   if (q == nullptr || q_blk == nullptr) return fail(LF_ERR_NULL, "q / q_blk is NULL");
-  const size_t need = (size_t)kg.B * kg.H * kg.Fh * kg.nb * kg.D * sizeof(double);
   if (kg.Fh > 0 && (k_cache == nullptr || k_blk == nullptr || k_frm == nullptr))
     return fail(LF_ERR_NULL, "k_cache / k_blk / k_frm is NULL");
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(LF_ERR_WORKSPACE, "workspace smaller than lf_compress_workspace_bytes()");
-  if (!aligned16(q) || !aligned16(q_blk) || (kg.Fh > 0 && (!aligned16(k_cache) || !aligned16(k_blk) ||
-                                                           !aligned16(k_frm) || !aligned16(workspace))))
+  if (!aligned16(q) || !aligned16(q_blk) ||
+      (kg.Fh > 0 && (!aligned16(k_cache) || !aligned16(k_blk) || !aligned16(k_frm))))
     return fail(LF_ERR_ALIGN, "pointers must be 16-byte aligned");
-  return hip_status(lf::launch_compress(kg, g->dtype, q, k_cache, q_blk, k_blk, k_frm,
-                                        static_cast<double*>(workspace), static_cast<hipStream_t>(stream)),
+  return hip_status(lf::launch_compress(kg, g->dtype, q, k_cache, q_blk, k_blk, k_frm, static_cast<hipStream_t>(stream)),
                     "lf_compress launch");
 }
 

@@ -22,7 +22,7 @@ struct KGeom {
 // Launchers (one per kernel family). They assume validated arguments and
 // return the HIP error of the launch.
 hipError_t launch_compress(const KGeom& g, int32_t dtype, const void* q, const void* k_cache, float* q_blk, float* k_blk,
-                           float* k_frm, double* blk_sum, hipStream_t stream);
+                           float* k_frm, hipStream_t stream);
 hipError_t launch_select(const KGeom& g, const float* q_blk, const float* k_blk, const float* k_frm,
                          int32_t kf, int32_t kb, int32_t k_frames_stride, int32_t* sel_frames,
                          int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, hipStream_t stream);

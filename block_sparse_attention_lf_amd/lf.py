@@ -25,10 +25,10 @@ LF_CACHE_ROLLING, LF_CACHE_ANCHORED = 0, 1
 LF_MAX_FRAMES, LF_MAX_BLOCKS_PER_FRAME, LF_MAX_BLOCK, LF_MAX_SEL = 256, 512, 128, 512
 
 STATUS = {0: "LF_OK", -1: "LF_ERR_NULL", -2: "LF_ERR_GEOM", -3: "LF_ERR_DTYPE", -4: "LF_ERR_K",
-          -5: "LF_ERR_ALIGN", -6: "LF_ERR_HIP", -7: "LF_ERR_WORKSPACE", -8: "LF_ERR_SLOT", -9: "LF_ERR_ARG"}
+          -5: "LF_ERR_ALIGN", -6: "LF_ERR_HIP", -7: "LF_ERR_SLOT", -8: "LF_ERR_ARG"}
 
 # Every symbol include/lf.h declares.
-EXPORTS = ("lf_compress_workspace_bytes", "lf_compress", "lf_max_sel", "lf_select", "lf_block_sparse_attn",
+EXPORTS = ("lf_compress", "lf_max_sel", "lf_select", "lf_block_sparse_attn",
            "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error")
 
 
@@ -71,8 +71,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     G = ctypes.POINTER(lf_geom)
     sig = {
-        "lf_compress_workspace_bytes": (ctypes.c_size_t, [G]),
-        "lf_compress": (ctypes.c_int, [G, _P, _P, _I32P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+        "lf_compress": (ctypes.c_int, [G, _P, _P, _I32P, _P, _P, _P, _P]),
         "lf_max_sel": (ctypes.c_int32, [G, ctypes.c_int32, ctypes.c_int32]),
         "lf_select": (ctypes.c_int, [G, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P]),
         "lf_block_sparse_attn": (ctypes.c_int, [G, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32, ctypes.c_float,
@@ -141,15 +140,11 @@ def _tdtype(g: lf_geom):
 # Entry points
 # --------------------------------------------------------------------------
 
-def lf_compress_workspace_bytes(g: lf_geom) -> int:
-    return int(lib().lf_compress_workspace_bytes(ctypes.byref(g)))
-
-
 def lf_max_sel(g: lf_geom, k_frames: int, k_blocks: int) -> int:
     return int(lib().lf_max_sel(ctypes.byref(g), k_frames, k_blocks))
 
 
-def lf_compress(g: lf_geom, q, k_cache, frame_slot, q_blk, k_blk, k_frm, workspace, stream=None) -> None:
+def lf_compress(g: lf_geom, q, k_cache, frame_slot, q_blk, k_blk, k_frm, stream=None) -> None:
     """Mean-pool query blocks and history key blocks/frames (see include/lf.h)."""
     D, nb = g.head_dim, g.blocks_per_frame
     _need(q, (g.batch, g.heads, g.q_len, D), _tdtype(g), "q")
@@ -158,9 +153,8 @@ def lf_compress(g: lf_geom, q, k_cache, frame_slot, q_blk, k_blk, k_frm, workspa
     _need(k_blk, (g.batch, g.heads, g.hist_frames * nb, D), torch.float32, "k_blk")
     _need(k_frm, (g.batch, g.heads, g.hist_frames, D), torch.float32, "k_frm")
     arr, sp = _slots(frame_slot)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().lf_compress(ctypes.byref(g), _ptr(q), _ptr(k_cache), sp, _ptr(q_blk), _ptr(k_blk), _ptr(k_frm),
-                             _ptr(workspace), ws_bytes, _stream(stream)), "lf_compress")
+                             _stream(stream)), "lf_compress")
 
 
 def lf_select(g: lf_geom, q_blk, k_blk, k_frm, k_frames: int, k_blocks: int, sel_frames, sel_blocks, n_sel,
@@ -247,8 +241,6 @@ class Buffers:
         self.q_blk = torch.empty((B, H, g.n_qblocks, D), dtype=f32, device=device)
         self.k_blk = torch.empty((B, H, g.hist_frames * nb, D), dtype=f32, device=device)
         self.k_frm = torch.empty((B, H, g.hist_frames, D), dtype=f32, device=device)
-        ws = lf_compress_workspace_bytes(g)
-        self.workspace = torch.empty((max(ws, 8) + 7) // 8, dtype=torch.float64, device=device)
         self.sel_frames = torch.empty((B, H, g.n_qblocks, k_frames), dtype=i32, device=device)
         self.sel_blocks = torch.empty((B, H, g.n_qblocks, self.max_sel), dtype=i32, device=device)
         self.n_sel = torch.empty((B, H, g.n_qblocks), dtype=i32, device=device)
@@ -260,7 +252,7 @@ def hsa_attention(g: lf_geom, q, k_cache, v_cache, frame_slot, bufs: Buffers, so
                   stream=None):
     """One hierarchical sparse attention call: compress -> select -> block-sparse attention."""
     scale = softmax_scale if softmax_scale is not None else 1.0 / float(np.sqrt(g.head_dim))
-    lf_compress(g, q, k_cache, frame_slot, bufs.q_blk, bufs.k_blk, bufs.k_frm, bufs.workspace, stream)
+    lf_compress(g, q, k_cache, frame_slot, bufs.q_blk, bufs.k_blk, bufs.k_frm, stream)
     lf_select(g, bufs.q_blk, bufs.k_blk, bufs.k_frm, bufs.k_frames, bufs.k_blocks, bufs.sel_frames, bufs.sel_blocks,
               bufs.n_sel, stream)
     lf_block_sparse_attn(g, q, k_cache, v_cache, frame_slot, bufs.sel_blocks, bufs.n_sel, scale, bufs.out, bufs.lse,

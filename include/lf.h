@@ -63,9 +63,8 @@ typedef enum {
   LF_ERR_K = -4,         /* top-k sizes / selection capacity invalid */
   LF_ERR_ALIGN = -5,     /* a device pointer is not 16-byte aligned */
   LF_ERR_HIP = -6,       /* the HIP runtime rejected a launch */
-  LF_ERR_WORKSPACE = -7, /* workspace missing or too small */
-  LF_ERR_SLOT = -8,      /* frame_slot entry out of range or repeated */
-  LF_ERR_ARG = -9        /* another argument out of range */
+  LF_ERR_SLOT = -7,      /* frame_slot entry out of range or repeated */
+  LF_ERR_ARG = -8        /* another argument out of range */
 } lf_status;
 
 typedef enum { LF_F32 = 0, LF_BF16 = 1 } lf_dtype;
@@ -101,15 +100,10 @@ typedef void* lf_stream; /* hipStream_t */
  * Mean pooling: q_blk[qb] = mean of the query block's tokens; k_blk[f*nb+j] =
  * mean of block j of history frame f; k_frm[f] = mean of all T tokens of
  * history frame f. Means are accumulated in float64 and rounded once to
- * float32 (mean = (float)(sum / count)).
- * `workspace` (device, >= lf_compress_workspace_bytes(g) bytes, 8-byte
- * aligned) holds the float64 block sums between the block and frame passes;
- * it may be NULL only when that size is 0. Its contents on entry are ignored.
+ * float32 (mean = (float)(sum / count)). One launch; no workspace.
  * ------------------------------------------------------------------------- */
-size_t lf_compress_workspace_bytes(const lf_geom* g);
 lf_status lf_compress(const lf_geom* g, const void* q, const void* k_cache, const int32_t* frame_slot,
-                      float* q_blk, float* k_blk, float* k_frm, void* workspace, size_t workspace_bytes,
-                      lf_stream stream);
+                      float* q_blk, float* k_blk, float* k_frm, lf_stream stream);
 
 /* ---------------------------------------------------------------------------
  * Two-stage mask selection ([LF-tech] 2.2 "two-stage mask selection";

@@ -34,7 +34,7 @@ def gpu_compress_select(w: I.Workload, x: dict, k_frames: int, k_blocks: int, de
     g = lf.geom_of(w)
     q, kc, vc = dev if dev is not None else device_inputs(w, x)
     bufs = lf.Buffers(g, k_frames, k_blocks, with_lse=True)
-    lf.lf_compress(g, q, kc, x["frame_slot"], bufs.q_blk, bufs.k_blk, bufs.k_frm, bufs.workspace)
+    lf.lf_compress(g, q, kc, x["frame_slot"], bufs.q_blk, bufs.k_blk, bufs.k_frm)
     lf.lf_select(g, bufs.q_blk, bufs.k_blk, bufs.k_frm, k_frames, k_blocks, bufs.sel_frames, bufs.sel_blocks,
                  bufs.n_sel)
     torch.cuda.synchronize()

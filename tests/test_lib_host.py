@@ -63,7 +63,7 @@ def test_chunk_budget_matches_oracle(variant):
 def test_chunk_budget_rejects_bad_sigma():
     with pytest.raises(lf.LfError) as e:
         lf.lf_chunk_budget([0.0, 1.0], None, [False, False], 0.9, 0.8, [1, 2], None, 5, 1)
-    assert e.value.status == -9
+    assert e.value.status == -8
 
 
 @pytest.mark.parametrize("policy,S,ns,Fc,c", [("rolling", 9, 0, 3, k) for k in range(7)] +
@@ -90,7 +90,7 @@ def _raw_compress(g, slots):
     L = lf.lib()
     fake = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
     return L.lf_compress(ctypes.byref(g), fake, fake, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                         fake, fake, fake, fake, 1 << 30, None)
+                         fake, fake, fake, None)
 
 
 @pytest.mark.parametrize("field,value,status", [("head_dim", 96, -2), ("dtype", 7, -3), ("block", 0, -2),
@@ -108,24 +108,23 @@ def test_bad_slot_tables_are_rejected():
     g = lf.geom_of(w)
     s = I.rotated_slots(w).copy()
     s[1] = s[0]
-    assert _raw_compress(g, s) == -8
+    assert _raw_compress(g, s) == -7
     s = I.rotated_slots(w).copy()
     s[2] = w.cache_slots
-    assert _raw_compress(g, s) == -8
+    assert _raw_compress(g, s) == -7
 
 
-def test_small_workspace_and_misalignment_are_rejected():
+def test_misalignment_and_null_are_rejected():
     w = I.WAN480P_CHUNK
     g = lf.geom_of(w)
     arr = I.rotated_slots(w)
     L = lf.lib()
     p = ctypes.c_void_p(4096)
     sp = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    assert L.lf_compress(ctypes.byref(g), p, p, sp, p, p, p, p, 8, None) == -7
     bad = ctypes.c_void_p(4096 + 8)
-    need = lf.lf_compress_workspace_bytes(g)
-    assert need == 12 * 6 * 25 * 128 * 8
-    assert L.lf_compress(ctypes.byref(g), bad, p, sp, p, p, p, p, need, None) == -5
+    assert L.lf_compress(ctypes.byref(g), bad, p, sp, p, p, p, None) == -5
+    assert L.lf_compress(ctypes.byref(g), p, p, sp, p, bad, p, None) == -5
+    assert L.lf_compress(ctypes.byref(g), p, None, sp, p, p, p, None) == -1
 
 
 def test_select_capacity_and_k_are_checked():
@@ -143,6 +142,6 @@ def test_attention_scale_and_nulls_are_checked():
     L = lf.lib()
     p = ctypes.c_void_p(4096)
     sp = I.rotated_slots(w).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    assert L.lf_block_sparse_attn(ctypes.byref(g), p, p, p, sp, p, p, 30, ctypes.c_float(0.0), p, None, None) == -9
+    assert L.lf_block_sparse_attn(ctypes.byref(g), p, p, p, sp, p, p, 30, ctypes.c_float(0.0), p, None, None) == -8
     assert L.lf_block_sparse_attn(ctypes.byref(g), p, None, p, sp, p, p, 30, ctypes.c_float(1.0), p, None, None) == -1
     assert L.lf_block_sparse_attn(ctypes.byref(g), p, p, p, sp, None, p, 30, ctypes.c_float(1.0), p, None, None) == -1
