@@ -17,9 +17,11 @@
 // NWAVE-th block of the frame (a frame of 25-29 blocks is then at most two
 // round trips to memory per wavefront), write its mean, and keep running
 // float64 column sums, which the workgroup adds up through LDS, in wavefront
-// order, into the frame mean. The remaining workgroups pool NWAVE query
-// blocks each. No partial result ever crosses workgroups, so there is no
-// second pass and no workspace.
+// order, into the frame mean. The remaining workgroups pool QWAVE query
+// blocks each (their other wavefronts leave at once): fewer blocks per
+// workgroup spread the queries over the CUs the frames leave idle. No partial
+// result ever crosses workgroups, so there is no second pass and no
+// workspace.
 #include "lf_internal.h"
 
 namespace lf {
@@ -101,9 +103,10 @@ struct BlockPool {
 };
 
 constexpr int NWAVE = 16;  // wavefronts per workgroup
+constexpr int QWAVE = 4;   // query blocks per query workgroup
 
 // Workgroups [0, B*H*Fh) own one history frame each, (b*H + h)*Fh + f; the
-// rest own NWAVE consecutive query blocks each. Output rows follow the
+// rest own QWAVE consecutive query blocks each. Output rows follow the
 // layouts: k_blk row (bh*Fh + f)*nb + j, k_frm row bh*Fh + f, q_blk row
 // bh*nqb + qb.
 template <typename T, int D>
@@ -148,8 +151,8 @@ __global__ __launch_bounds__(64 * NWAVE) void pool_kernel(const T* __restrict__ 
     return;
   }
 
-  const int64_t it = (wg - n_frames) * NWAVE + wv;  // query block item, (b*H + h)*nqb + qb
-  if (it >= (int64_t)g.B * g.H * g.nqb) return;  // whole wave leaves; no barriers on this path
+  const int64_t it = (wg - n_frames) * QWAVE + wv;  // query block item, (b*H + h)*nqb + qb
+  if (wv >= QWAVE || it >= (int64_t)g.B * g.H * g.nqb) return;  // whole wave leaves; no barriers on this path
   const int64_t bh = it / g.nqb;
   const int qb = (int)(it - bh * g.nqb);
   const int fc = qb / g.nb, j = qb - fc * g.nb;
@@ -162,7 +165,7 @@ template <typename T, int D>
 hipError_t launch_typed(const KGeom& g, const void* q, const void* k, float* q_blk, float* k_blk, float* k_frm,
                         hipStream_t stream) {
   const int64_t n_frames = (int64_t)g.B * g.H * g.Fh;
-  const int64_t n_q = ((int64_t)g.B * g.H * g.nqb + NWAVE - 1) / NWAVE;
+  const int64_t n_q = ((int64_t)g.B * g.H * g.nqb + QWAVE - 1) / QWAVE;
   hipLaunchKernelGGL((pool_kernel<T, D>), dim3((unsigned)(n_frames + n_q)), dim3(64 * NWAVE), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), q_blk, k_blk, k_frm, g);
   return hipGetLastError();
