@@ -118,6 +118,33 @@ int32_t lf_max_sel(const lf_geom* g, int32_t k_frames, int32_t k_blocks) {
   return (int32_t)max_sel_of(kg, k_frames, k_blocks);
 }
 
+int32_t lf_max_sel_1d(const lf_geom* g, int32_t k_total) {
+  lf::KGeom kg;
+  if (make_geom(g, nullptr, &kg) != LF_OK || k_total < 0) return -1;
+  const int64_t ncand = (int64_t)(kg.Fh - kg.ns) * kg.nb;
+  return (int32_t)((int64_t)kg.ns * kg.nb + (k_total < ncand ? k_total : ncand));
+}
+
+lf_status lf_select_blocks(const lf_geom* g, const float* q_blk, const float* k_blk, int32_t k_total,
+                           int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, lf_stream stream) {
+  lf::KGeom kg;
+  lf_status st = make_geom(g, nullptr, &kg);
+  if (st != LF_OK) return st;
+  if (k_total < 0) return fail(LF_ERR_K, "k_total must be >= 0");
+  const int64_t ncand = (int64_t)(kg.Fh - kg.ns) * kg.nb;
+  if (ncand > LF_MAX_CANDIDATES_1D) return fail(LF_ERR_GEOM, "more than LF_MAX_CANDIDATES_1D candidate blocks");
+  const int k = (int)(k_total < ncand ? k_total : ncand);
+  if (max_sel < (int64_t)kg.ns * kg.nb + k) return fail(LF_ERR_K, "max_sel smaller than lf_max_sel_1d()");
+  if (q_blk == nullptr || n_sel == nullptr || (max_sel > 0 && sel_blocks == nullptr))
+    return fail(LF_ERR_NULL, "q_blk / sel_blocks / n_sel is NULL");
+  if (kg.Fh > 0 && k_blk == nullptr) return fail(LF_ERR_NULL, "k_blk is NULL");
+  if (!aligned16(q_blk) || (kg.Fh > 0 && !aligned16(k_blk)))
+    return fail(LF_ERR_ALIGN, "pooled tensors must be 16-byte aligned");
+  return hip_status(lf::launch_select_blocks(kg, q_blk, k_blk, k, sel_blocks, n_sel, max_sel,
+                                             static_cast<hipStream_t>(stream)),
+                    "lf_select_blocks launch");
+}
+
 lf_status lf_select(const lf_geom* g, const float* q_blk, const float* k_blk, const float* k_frm, int32_t k_frames,
                     int32_t k_blocks, int32_t* sel_frames, int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel,
                     lf_stream stream) {

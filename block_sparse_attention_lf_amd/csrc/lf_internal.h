@@ -26,6 +26,8 @@ hipError_t launch_compress(const KGeom& g, int32_t dtype, const void* q, const v
 hipError_t launch_select(const KGeom& g, const float* q_blk, const float* k_blk, const float* k_frm,
                          int32_t kf, int32_t kb, int32_t k_frames_stride, int32_t* sel_frames,
                          int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, hipStream_t stream);
+hipError_t launch_select_blocks(const KGeom& g, const float* q_blk, const float* k_blk, int32_t k,
+                                int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, hipStream_t stream);
 hipError_t launch_attention(const KGeom& g, int32_t dtype, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel, float scale,
                             void* out, float* lse, hipStream_t stream);

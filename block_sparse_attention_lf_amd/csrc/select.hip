@@ -106,6 +106,79 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
   if (lane == 0) n_sel[item] = pos;
 }
 
+// Order-preserving map of a float64 score to an unsigned key (larger score,
+// larger key; inputs are finite).
+__device__ inline uint64_t score_key(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u >> 63) ? ~u : (u | (1ull << 63));
+}
+
+// Single-level ("1D") selection (press summary, section 4, the ablation
+// baseline): one top-k over every non-sink history block, no frame stage.
+// One wavefront per query block. Scores go to LDS as order-preserving keys;
+// the k-th largest key T is found bit by bit from the top (is there at least
+// k keys >= T | bit?), each count a sum of ballots; then keys > T are kept
+// and keys == T fill the rest in ascending index, i.e. exactly "stable sort
+// descending, take the first k". Ids ascend by construction.
+template <int D>
+__global__ __launch_bounds__(64) void select_blocks_kernel(const float* __restrict__ q_blk,
+                                                           const float* __restrict__ k_blk, const KGeom g, int k,
+                                                           int32_t* __restrict__ sel_blocks,
+                                                           int32_t* __restrict__ n_sel, int max_sel) {
+  __shared__ __attribute__((aligned(16))) float qv[D];
+  __shared__ uint64_t key[LF_MAX_CANDIDATES_1D];
+
+  const int lane = threadIdx.x;
+  const int64_t item = blockIdx.x;  // (b*H + h)*nqb + qb
+  const int64_t bh = item / g.nqb;
+  const int nb = g.nb, ns = g.ns;
+  for (int d = lane; d < D; d += 64) qv[d] = q_blk[item * D + d];
+  __syncthreads();
+
+  int32_t* out = sel_blocks + item * max_sel;
+  for (int i = lane; i < ns * nb; i += 64) out[i] = i;  // sink frames in full
+  const int base = ns * nb;
+  const int ncand = (g.Fh - ns) * nb;
+  const float* rows = k_blk + (bh * g.Fh + ns) * (int64_t)nb * D;
+  for (int c = lane; c < ncand; c += 64) key[c] = score_key(dot_f64<D>(qv, rows + (int64_t)c * D));
+  __syncthreads();
+
+  // k-th largest key
+  uint64_t t = 0;
+  if (k > 0) {
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cand = t | (1ull << bit);
+      int cnt = 0;
+      for (int c0 = 0; c0 < ncand; c0 += 64) {
+        const int c = c0 + lane;
+        cnt += __popcll(__ballot(c < ncand && key[c] >= cand));
+      }
+      if (cnt >= k) t = cand;
+    }
+  }
+  int above = 0;  // keys strictly above t
+  for (int c0 = 0; c0 < ncand; c0 += 64) {
+    const int c = c0 + lane;
+    above += __popcll(__ballot(k > 0 && c < ncand && key[c] > t));
+  }
+  int pos = base, ties_left = k - above;
+  for (int c0 = 0; c0 < ncand; c0 += 64) {
+    const int c = c0 + lane;
+    const bool valid = k > 0 && c < ncand;
+    const bool tie = valid && key[c] == t;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    const unsigned long long tm = __ballot(tie);
+    const bool take = valid && (key[c] > t || (tie && __popcll(tm & lt) < ties_left));
+    const unsigned long long m = __ballot(take);
+    const int at = pos + __popcll(m & lt);
+    if (take && at < max_sel) out[at] = base + c;
+    pos = min(pos + __popcll(m), max_sel);
+    ties_left -= min(__popcll(tm), max(ties_left, 0));
+  }
+  for (int i = pos + lane; i < max_sel; i += 64) out[i] = -1;
+  if (lane == 0) n_sel[item] = pos;
+}
+
 }  // namespace
 
 hipError_t launch_select(const KGeom& g, const float* q_blk, const float* k_blk, const float* k_frm, int32_t kf,
@@ -118,6 +191,18 @@ hipError_t launch_select(const KGeom& g, const float* q_blk, const float* k_blk,
   else
     hipLaunchKernelGGL((select_kernel<64>), dim3(grid), dim3(64), 0, stream, q_blk, k_blk, k_frm, g, kf, kb,
                        k_frames_stride, sel_frames, sel_blocks, n_sel, max_sel);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_blocks(const KGeom& g, const float* q_blk, const float* k_blk, int32_t k,
+                                int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, hipStream_t stream) {
+  const unsigned grid = (unsigned)((int64_t)g.B * g.H * g.nqb);
+  if (g.D == 128)
+    hipLaunchKernelGGL((select_blocks_kernel<128>), dim3(grid), dim3(64), 0, stream, q_blk, k_blk, g, k, sel_blocks,
+                       n_sel, max_sel);
+  else
+    hipLaunchKernelGGL((select_blocks_kernel<64>), dim3(grid), dim3(64), 0, stream, q_blk, k_blk, g, k, sel_blocks,
+                       n_sel, max_sel);
   return hipGetLastError();
 }
 

@@ -22,13 +22,13 @@ LIB_PATH = os.path.join(HERE, "liblf.so")
 
 LF_F32, LF_BF16 = 0, 1
 LF_CACHE_ROLLING, LF_CACHE_ANCHORED = 0, 1
-LF_MAX_FRAMES, LF_MAX_BLOCKS_PER_FRAME, LF_MAX_BLOCK, LF_MAX_SEL = 256, 512, 128, 512
+LF_MAX_FRAMES, LF_MAX_BLOCKS_PER_FRAME, LF_MAX_BLOCK, LF_MAX_SEL, LF_MAX_CANDIDATES_1D = 256, 512, 128, 512, 4096
 
 STATUS = {0: "LF_OK", -1: "LF_ERR_NULL", -2: "LF_ERR_GEOM", -3: "LF_ERR_DTYPE", -4: "LF_ERR_K",
           -5: "LF_ERR_ALIGN", -6: "LF_ERR_HIP", -7: "LF_ERR_SLOT", -8: "LF_ERR_ARG"}
 
 # Every symbol include/lf.h declares.
-EXPORTS = ("lf_compress", "lf_max_sel", "lf_select", "lf_block_sparse_attn",
+EXPORTS = ("lf_compress", "lf_max_sel", "lf_select", "lf_max_sel_1d", "lf_select_blocks", "lf_block_sparse_attn",
            "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error")
 
 
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         "lf_compress": (ctypes.c_int, [G, _P, _P, _I32P, _P, _P, _P, _P]),
         "lf_max_sel": (ctypes.c_int32, [G, ctypes.c_int32, ctypes.c_int32]),
         "lf_select": (ctypes.c_int, [G, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P]),
+        "lf_max_sel_1d": (ctypes.c_int32, [G, ctypes.c_int32]),
+        "lf_select_blocks": (ctypes.c_int, [G, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P]),
         "lf_block_sparse_attn": (ctypes.c_int, [G, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32, ctypes.c_float,
                                                 _P, _P, _P]),
         "lf_chunk_budget": (ctypes.c_int, [ctypes.c_int32, _F64P, _F64P, ctypes.POINTER(ctypes.c_uint8),
@@ -171,6 +173,22 @@ def lf_select(g: lf_geom, q_blk, k_blk, k_frm, k_frames: int, k_blocks: int, sel
         _need(sel_frames, (g.batch, g.heads, g.n_qblocks, k_frames), torch.int32, "sel_frames")
     _check(lib().lf_select(ctypes.byref(g), _ptr(q_blk), _ptr(k_blk), _ptr(k_frm), k_frames, k_blocks,
                            _ptr(sel_frames), _ptr(sel_blocks), _ptr(n_sel), max_sel, _stream(stream)), "lf_select")
+
+
+def lf_max_sel_1d(g: lf_geom, k_total: int) -> int:
+    return int(lib().lf_max_sel_1d(ctypes.byref(g), k_total))
+
+
+def lf_select_blocks(g: lf_geom, q_blk, k_blk, k_total: int, sel_blocks, n_sel, stream=None) -> None:
+    """Single-level ("1D") block top-k over all non-sink history blocks (see include/lf.h)."""
+    D, nb = g.head_dim, g.blocks_per_frame
+    _need(q_blk, (g.batch, g.heads, g.n_qblocks, D), torch.float32, "q_blk")
+    _need(k_blk, (g.batch, g.heads, g.hist_frames * nb, D), torch.float32, "k_blk")
+    max_sel = sel_blocks.shape[-1]
+    _need(sel_blocks, (g.batch, g.heads, g.n_qblocks, max_sel), torch.int32, "sel_blocks")
+    _need(n_sel, (g.batch, g.heads, g.n_qblocks), torch.int32, "n_sel")
+    _check(lib().lf_select_blocks(ctypes.byref(g), _ptr(q_blk), _ptr(k_blk), k_total, _ptr(sel_blocks), _ptr(n_sel),
+                                  max_sel, _stream(stream)), "lf_select_blocks")
 
 
 def lf_block_sparse_attn(g: lf_geom, q, k_cache, v_cache, frame_slot, sel_blocks, n_sel, softmax_scale: float, out,

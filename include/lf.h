@@ -79,6 +79,8 @@ typedef enum { LF_CACHE_ROLLING = 0, LF_CACHE_ANCHORED = 1 } lf_cache_policy;
 #define LF_MAX_BLOCK 128
 /* Most selected blocks per query block the attention kernel reads (max_sel). */
 #define LF_MAX_SEL 512
+/* Most candidate blocks ((Fh - n_sink) * nb) the single-level selection ranks. */
+#define LF_MAX_CANDIDATES_1D 4096
 
 typedef struct {
   int32_t batch;            /* B >= 1 */
@@ -124,6 +126,23 @@ int32_t lf_max_sel(const lf_geom* g, int32_t k_frames, int32_t k_blocks);
 lf_status lf_select(const lf_geom* g, const float* q_blk, const float* k_blk, const float* k_frm,
                     int32_t k_frames, int32_t k_blocks, int32_t* sel_frames, int32_t* sel_blocks,
                     int32_t* n_sel, int32_t max_sel, lf_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * Single-level ("1D") selection, the ablation baseline ([LF-press] 4,
+ * ablation paragraph: block sparse attention without the frame stage). Per
+ * (batch, head, query block): block score <q_blk, k_blk[id]> in float64 for
+ * every block of the non-sink history frames; keep the k = min(k_total,
+ * candidates) largest (ties to the lower id); selected ids = all blocks of
+ * the sink frames + the kept ids, ascending. With k_total = k_frames *
+ * k_blocks it spends the same block budget as lf_select. Outputs as
+ * lf_select's sel_blocks / n_sel. max_sel must be >= lf_max_sel_1d(g,
+ * k_total); (Fh - n_sink) * nb must be <= LF_MAX_CANDIDATES_1D. The uniform
+ * allocation baseline needs no entry point: lf_chunk_budget with s_target ==
+ * s_base gives beta = 0, the same sparsity for every chunk.
+ * ------------------------------------------------------------------------- */
+int32_t lf_max_sel_1d(const lf_geom* g, int32_t k_total);
+lf_status lf_select_blocks(const lf_geom* g, const float* q_blk, const float* k_blk, int32_t k_total,
+                           int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, lf_stream stream);
 
 /* ---------------------------------------------------------------------------
  * Block-sparse attention ([LF-tech] 2.2 "execution"; [LF-press] 3).

@@ -32,7 +32,9 @@ Readings where the pages leave a step open (each restated at its function):
   R6 the current chunk sees all of its own tokens (chunk-granular causality);
   R7 softmax scale 1/sqrt(d), a parameter;
   R8 sink frames are always attended in full and are not top-k candidates;
-  R15 ties in a top-k go to the lowest index.
+  R15 ties in a top-k go to the lowest index;
+  R18 the single-level ("1D") ablation variant ranks all non-sink history
+      blocks in one top-k.
 Pooling sums in float64 and rounds the mean once to float32; scores are
 float64 dot products of those float32 values; attention is float64 dense
 masked softmax.
@@ -173,6 +175,46 @@ def select(q_blk: np.ndarray, k_blk: np.ndarray, k_frm: np.ndarray, hist_frames:
                 sel_blocks[b, h, qb, :len(ids)] = ids
     return {"sel_frames": sel_frames, "sel_blocks": sel_blocks, "n_sel": n_sel,
             "frame_scores": frame_scores, "block_scores": block_scores}
+
+
+def max_selected_1d(hist_frames: int, n_sink: int, blocks_per_frame: int, k_total: int) -> int:
+    ns = min(n_sink, hist_frames)
+    return ns * blocks_per_frame + max(0, min(k_total, (hist_frames - ns) * blocks_per_frame))
+
+
+def select_blocks(q_blk: np.ndarray, k_blk: np.ndarray, hist_frames: int, n_sink: int, blocks_per_frame: int,
+                  k_total: int) -> Dict[str, np.ndarray]:
+    """Single-level ("1D") selection: one top-k over every non-sink history block.
+
+    The ablation baseline of the press summary, section 4 (ablation
+    paragraph): block sparse attention without the frame stage. Reading R18:
+    the candidates are all blocks of the non-sink history frames, scored
+    <q_blk[qb], k_blk[id]> in float64 exactly as in select(); the k_total best
+    are kept (ties to the lowest id, R15), k_total clamped to the candidate
+    count; sink frames are attended in full (R8); ids ascending. With
+    k_total = k_frames * k_blocks both variants spend the same block budget.
+    Pinned by tests/test_oracle_select.py (brute force, a plant the frame
+    stage cannot follow, the all-blocks limit).
+    """
+    B, H, nqb, d = q_blk.shape
+    nb = blocks_per_frame
+    ns = min(n_sink, hist_frames)
+    cands = list(range(ns * nb, hist_frames * nb))
+    k = max(0, min(k_total, len(cands)))
+    m = ns * nb + k
+    sel_blocks = np.full((B, H, nqb, max(m, 1)), -1, np.int32)
+    n_sel = np.zeros((B, H, nqb), np.int32)
+    scores = np.zeros((B, H, nqb, len(cands)), np.float64)
+    for b in range(B):
+        for h in range(H):
+            for qb in range(nqb):
+                qv = q_blk[b, h, qb].astype(np.float64)
+                sc = np.array([np.dot(qv, k_blk[b, h, i].astype(np.float64)) for i in cands], np.float64)
+                scores[b, h, qb] = sc
+                ids = list(range(ns * nb)) + sorted(cands[int(i)] for i in top_k_desc(sc, k))
+                n_sel[b, h, qb] = len(ids)
+                sel_blocks[b, h, qb, :len(ids)] = ids
+    return {"sel_blocks": sel_blocks, "n_sel": n_sel, "scores": scores}
 
 
 # ---------------------------------------------------------------------------

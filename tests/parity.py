@@ -146,3 +146,34 @@ def compare_attention(w: I.Workload, x: dict, out: np.ndarray, lse: np.ndarray, 
     assert stats["rel_l2"] <= REL_L2, stats
     assert stats["lse_abs"] <= LSE_ABS, stats
     return stats
+
+
+def gpu_select_blocks(g, bufs, k_total: int):
+    """Single-level selection on the GPU from already pooled q_blk / k_blk in bufs."""
+    m = max(lf.lf_max_sel_1d(g, k_total), 1)
+    sel = torch.empty((g.batch, g.heads, g.n_qblocks, m), dtype=torch.int32, device="cuda")
+    n = torch.empty((g.batch, g.heads, g.n_qblocks), dtype=torch.int32, device="cuda")
+    lf.lf_select_blocks(g, bufs.q_blk, bufs.k_blk, k_total, sel, n)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), n.cpu().numpy()
+
+
+def compare_selection_1d(g_sel, g_n, r: dict, k_total: int):
+    """Returns (n_checked, n_excused, unexcused mismatches) for the single-level variant."""
+    r_sel, r_n, sc = r["sel_blocks"], r["n_sel"], r["scores"]
+    k = min(k_total, sc.shape[-1])
+    B, H, nqb = r_n.shape
+    excused, bad = 0, []
+    for b in range(B):
+        for h in range(H):
+            for qb in range(nqb):
+                n = r_n[b, h, qb]
+                same = g_n[b, h, qb] == n and np.array_equal(g_sel[b, h, qb, :n], r_sel[b, h, qb, :n])
+                same = same and np.all(g_sel[b, h, qb, n:] == -1)
+                if same:
+                    continue
+                if _boundary_tie(sc[b, h, qb], k):
+                    excused += 1
+                    continue
+                bad.append((b, h, qb, g_sel[b, h, qb, :g_n[b, h, qb]].tolist(), r_sel[b, h, qb, :n].tolist()))
+    return B * H * nqb, excused, bad

@@ -145,3 +145,19 @@ def test_attention_scale_and_nulls_are_checked():
     assert L.lf_block_sparse_attn(ctypes.byref(g), p, p, p, sp, p, p, 30, ctypes.c_float(0.0), p, None, None) == -8
     assert L.lf_block_sparse_attn(ctypes.byref(g), p, None, p, sp, p, p, 30, ctypes.c_float(1.0), p, None, None) == -1
     assert L.lf_block_sparse_attn(ctypes.byref(g), p, p, p, sp, None, p, 30, ctypes.c_float(1.0), p, None, None) == -1
+
+
+def test_select_blocks_validation():
+    w = I.WAN480P_CHUNK
+    g = lf.geom_of(w)
+    L = lf.lib()
+    p = ctypes.c_void_p(4096)
+    nb = w.blocks_per_frame
+    assert lf.lf_max_sel_1d(g, 30) == 30
+    assert lf.lf_max_sel_1d(g, 10 ** 6) == w.hist_frames * nb
+    assert lf.lf_max_sel_1d(g, -1) == -1
+    assert L.lf_select_blocks(ctypes.byref(g), p, p, -1, p, p, 30, None) == -4
+    assert L.lf_select_blocks(ctypes.byref(g), p, p, 30, p, p, 29, None) == -4
+    assert L.lf_select_blocks(ctypes.byref(g), None, p, 30, p, p, 30, None) == -1
+    big = lf.geom_of(I.WAN480P_CHUNK.replace(hist_frames=200, cache_slots=203, block=16))
+    assert L.lf_select_blocks(ctypes.byref(big), p, p, 30, p, p, 10 ** 6, None) == -2

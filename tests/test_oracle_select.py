@@ -146,3 +146,72 @@ def test_invariant_to_common_key_shift_and_power_of_two_query_scale():
     c = np.float32(0.5) * np.sign(rng.standard_normal(d)).astype(np.float32)
     shifted = O.select(q, kb + c, kf + c, F, 0, nb, 3, 2)
     assert np.array_equal(base["sel_blocks"], shifted["sel_blocks"])
+
+
+# ---------------------------------------------------------------------------
+# Single-level ("1D") selection, the ablation baseline (press summary,
+# section 4): one top-k over all non-sink history blocks.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(12))
+def test_select_blocks_matches_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    Fh, nb, d = 4, 3, 4
+    ns = int(seed % 2)
+    q_blk = rng.integers(-2, 3, size=(1, 1, 2, d)).astype(np.float32)
+    k_blk = rng.integers(-2, 3, size=(1, 1, Fh * nb, d)).astype(np.float32)  # integer grid: many exact ties
+    ncand = (Fh - ns) * nb
+    for k in range(ncand + 2):
+        r = O.select_blocks(q_blk, k_blk, Fh, ns, nb, k)
+        for qb in range(2):
+            sc = [float(np.dot(q_blk[0, 0, qb].astype(np.float64), k_blk[0, 0, i].astype(np.float64)))
+                  for i in range(ns * nb, Fh * nb)]
+            want = list(range(ns * nb)) + sorted(ns * nb + i for i in brute_top_k(sc, min(k, ncand)))
+            n = int(r["n_sel"][0, 0, qb])
+            assert r["sel_blocks"][0, 0, qb, :n].tolist() == want
+
+
+def test_select_blocks_follows_a_plant_the_frame_stage_cannot():
+    """All four best blocks sit in one frame: the single-level top-4 takes them
+    all, while the two-stage selection with the same budget (2 frames x 2
+    blocks) can take only two of them."""
+    Fh, nb, d = 4, 4, 8
+    rng = np.random.default_rng(7)
+    q_blk = np.zeros((1, 1, 1, d), np.float32)
+    q_blk[..., 0] = 1.0
+    k_blk = rng.normal(0, 0.1, size=(1, 1, Fh * nb, d)).astype(np.float32)
+    k_blk[0, 0, 2 * nb:3 * nb, 0] += 5.0          # frame 2's blocks dominate
+    k_frm = k_blk.reshape(1, 1, Fh, nb, d).mean(axis=3).astype(np.float32)
+    one = O.select_blocks(q_blk, k_blk, Fh, 0, nb, 4)
+    assert one["sel_blocks"][0, 0, 0].tolist() == list(range(2 * nb, 3 * nb))
+    two = O.select(q_blk, k_blk, k_frm, Fh, 0, nb, 2, 2)
+    got = set(two["sel_blocks"][0, 0, 0, :int(two["n_sel"][0, 0, 0])].tolist())
+    assert len(got & set(range(2 * nb, 3 * nb))) == 2 and len(got) == 4
+
+
+def test_select_blocks_all_blocks_and_sinks():
+    rng = np.random.default_rng(3)
+    Fh, nb, d, ns = 5, 4, 8, 2
+    q_blk = rng.normal(size=(1, 2, 3, d)).astype(np.float32)
+    k_blk = rng.normal(size=(1, 2, Fh * nb, d)).astype(np.float32)
+    r = O.select_blocks(q_blk, k_blk, Fh, ns, nb, 10 ** 6)
+    assert (r["n_sel"] == Fh * nb).all()
+    assert (r["sel_blocks"] == np.arange(Fh * nb)).all()
+    assert O.max_selected_1d(Fh, ns, nb, 5) == ns * nb + 5
+    r0 = O.select_blocks(q_blk, k_blk, Fh, ns, nb, 0)
+    assert (r0["n_sel"] == ns * nb).all()
+
+
+def test_select_blocks_invariant_to_common_key_shift():
+    rng = np.random.default_rng(11)
+    Fh, nb, d = 6, 5, 16
+    q_blk = rng.normal(size=(1, 1, 4, d)).astype(np.float32)
+    k_blk = rng.normal(size=(1, 1, Fh * nb, d)).astype(np.float32)
+    shift = rng.normal(size=(d,)).astype(np.float32)
+    a = O.select_blocks(q_blk, k_blk, Fh, 1, nb, 7)
+    b = O.select_blocks(q_blk, (k_blk + shift).astype(np.float32), Fh, 1, nb, 7)
+    # scores move by <q, shift> for every candidate alike: same selection unless
+    # float32 rounding of the shifted keys reorders a near-tie
+    gaps = np.diff(np.sort(a["scores"], axis=-1), axis=-1)
+    if np.min(gaps) > 1e-3:
+        assert np.array_equal(a["sel_blocks"], b["sel_blocks"])
