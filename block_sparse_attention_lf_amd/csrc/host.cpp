@@ -118,6 +118,49 @@ int32_t lf_max_sel(const lf_geom* g, int32_t k_frames, int32_t k_blocks) {
   return (int32_t)max_sel_of(kg, k_frames, k_blocks);
 }
 
+lf_status lf_pool_keys(const lf_geom* g, const void* k_cache, const int32_t* slots, int32_t n_slots, float* kp_blk,
+                       float* kp_frm, lf_stream stream) {
+  lf::KGeom kg;
+  lf_status st = make_geom(g, nullptr, &kg);
+  if (st != LF_OK) return st;
+  if (n_slots < 0 || n_slots > LF_MAX_FRAMES) return fail(LF_ERR_ARG, "n_slots must be in [0, LF_MAX_FRAMES]");
+  if (n_slots == 0) return LF_OK;
+  if (slots == nullptr || k_cache == nullptr || kp_blk == nullptr || kp_frm == nullptr)
+    return fail(LF_ERR_NULL, "slots / k_cache / kp_blk / kp_frm is NULL");
+  for (int i = 0; i < n_slots; ++i) {
+    if (slots[i] < 0 || slots[i] >= kg.S) return fail(LF_ERR_SLOT, "slot outside [0, cache_slots)");
+    for (int j = 0; j < i; ++j)
+      if (slots[j] == slots[i]) return fail(LF_ERR_SLOT, "slot named twice");
+    kg.slot[i] = slots[i];
+  }
+  kg.Fh = n_slots;
+  if (!aligned16(k_cache) || !aligned16(kp_blk) || !aligned16(kp_frm))
+    return fail(LF_ERR_ALIGN, "pointers must be 16-byte aligned");
+  return hip_status(lf::launch_pool_slots(kg, g->dtype, k_cache, kp_blk, kp_frm, static_cast<hipStream_t>(stream)),
+                    "lf_pool_keys launch");
+}
+
+lf_status lf_select_fused(const lf_geom* g, const void* q, const float* kp_blk, const float* kp_frm,
+                          const int32_t* frame_slot, int32_t k_frames, int32_t k_blocks, int32_t* sel_frames,
+                          int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, float* q_blk, lf_stream stream) {
+  if (frame_slot == nullptr) return fail(LF_ERR_NULL, "frame_slot is NULL");
+  lf::KGeom kg;
+  lf_status st = make_geom(g, frame_slot, &kg);
+  if (st != LF_OK) return st;
+  if (k_frames < 0 || k_blocks < 0) return fail(LF_ERR_K, "k_frames and k_blocks must be >= 0");
+  if (max_sel < max_sel_of(kg, k_frames, k_blocks)) return fail(LF_ERR_K, "max_sel smaller than lf_max_sel()");
+  if (q == nullptr || n_sel == nullptr || (max_sel > 0 && sel_blocks == nullptr))
+    return fail(LF_ERR_NULL, "q / sel_blocks / n_sel is NULL");
+  if (kg.Fh > 0 && (kp_blk == nullptr || kp_frm == nullptr)) return fail(LF_ERR_NULL, "kp_blk / kp_frm is NULL");
+  if (!aligned16(q) || !aligned16(q_blk) || (kg.Fh > 0 && (!aligned16(kp_blk) || !aligned16(kp_frm))))
+    return fail(LF_ERR_ALIGN, "pointers must be 16-byte aligned");
+  const int kf = k_frames < kg.Fh - kg.ns ? k_frames : kg.Fh - kg.ns;
+  const int kb = k_blocks < kg.nb ? k_blocks : kg.nb;
+  return hip_status(lf::launch_select_fused(kg, g->dtype, q, kp_blk, kp_frm, kf, kb, k_frames, sel_frames, sel_blocks,
+                                            n_sel, max_sel, q_blk, static_cast<hipStream_t>(stream)),
+                    "lf_select_fused launch");
+}
+
 int32_t lf_max_sel_1d(const lf_geom* g, int32_t k_total) {
   lf::KGeom kg;
   if (make_geom(g, nullptr, &kg) != LF_OK || k_total < 0) return -1;

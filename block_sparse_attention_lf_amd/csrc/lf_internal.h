@@ -23,9 +23,16 @@ struct KGeom {
 // return the HIP error of the launch.
 hipError_t launch_compress(const KGeom& g, int32_t dtype, const void* q, const void* k_cache, float* q_blk, float* k_blk,
                            float* k_frm, hipStream_t stream);
+// Pools the frames in cache slots g.slot[0..g.Fh) into slot-indexed pooled caches.
+hipError_t launch_pool_slots(const KGeom& g, int32_t dtype, const void* k_cache, float* kp_blk, float* kp_frm,
+                             hipStream_t stream);
 hipError_t launch_select(const KGeom& g, const float* q_blk, const float* k_blk, const float* k_frm,
                          int32_t kf, int32_t kb, int32_t k_frames_stride, int32_t* sel_frames,
                          int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, hipStream_t stream);
+hipError_t launch_select_fused(const KGeom& g, int32_t dtype, const void* q, const float* kp_blk, const float* kp_frm,
+                               int32_t kf, int32_t kb, int32_t k_frames_stride, int32_t* sel_frames,
+                               int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, float* q_blk,
+                               hipStream_t stream);
 hipError_t launch_select_blocks(const KGeom& g, const float* q_blk, const float* k_blk, int32_t k,
                                 int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, hipStream_t stream);
 hipError_t launch_attention(const KGeom& g, int32_t dtype, const void* q, const void* k_cache, const void* v_cache,

@@ -17,7 +17,7 @@
 // ids are compacted in ascending order with a ballot and a prefix popcount.
 // The whole step reads O(kf*nb + Fh) pooled vectors per query block,
 // independent of how long the history is beyond that.
-#include "lf_internal.h"
+#include "pool.h"
 
 namespace lf {
 namespace {
@@ -49,12 +49,24 @@ __device__ inline void rank_keep(const double* score, int n, int k, unsigned cha
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_blk, const float* __restrict__ k_blk,
-                                                    const float* __restrict__ k_frm, const KGeom g, int kf, int kb,
-                                                    int kf_stride, int32_t* __restrict__ sel_frames,
+// Pooled-key row of history frame f: per logical frame (bh*Fh + f) as
+// lf_compress writes them, or per cache slot (bh*S + slot[f]) as the
+// commit-time pooling keeps them.
+__device__ inline int64_t key_row(bool by_slot, const KGeom& g, int64_t bh, int f) {
+  return by_slot ? bh * g.S + g.slot[f] : bh * g.Fh + f;
+}
+
+// FUSED = false: pooled queries q_blk and pooled keys per logical history
+// frame, as lf_compress writes them. FUSED = true: the query block is pooled
+// here from q (and optionally written to q_blk_out), and the pooled keys come
+// from the slot-indexed cache filled on commit.
+template <int D, bool FUSED, typename T>
+__global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_blk, const T* __restrict__ q,
+                                                    const float* __restrict__ k_blk, const float* __restrict__ k_frm,
+                                                    const KGeom g, int kf, int kb, int kf_stride,
+                                                    int32_t* __restrict__ sel_frames,
                                                     int32_t* __restrict__ sel_blocks, int32_t* __restrict__ n_sel,
-                                                    int max_sel) {
+                                                    int max_sel, float* __restrict__ q_blk_out) {
   __shared__ float qv[D];
   __shared__ double fscore[LF_MAX_FRAMES];
   __shared__ unsigned char fkeep[LF_MAX_FRAMES];
@@ -65,7 +77,21 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
   const int64_t item = blockIdx.x;  // (b*H + h)*nqb + qb
   const int64_t bh = item / g.nqb;
   const int nb = g.nb, ns = g.ns;
-  for (int d = lane; d < D; d += 64) qv[d] = q_blk[item * D + d];
+  if constexpr (FUSED) {
+    using P = BlockPool<T, D>;
+    const int qb = (int)(item - bh * g.nqb);
+    const int fc = qb / nb, jq = qb - fc * nb;
+    const int rows = min(g.b, g.T - jq * g.b);
+    double acc[P::EPL];
+    P::sums(q + (bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b) * D, rows, lane, acc);
+    if (lane < P::LPR) {
+#pragma unroll
+      for (int e = 0; e < P::EPL; ++e) qv[lane * P::EPL + e] = (float)(acc[e] / (double)rows);
+    }
+    if (q_blk_out != nullptr) P::store_mean(q_blk_out + item * D, acc, rows, lane);
+  } else {
+    for (int d = lane; d < D; d += 64) qv[d] = q_blk[item * D + d];
+  }
   __syncthreads();
 
   int32_t* out = sel_blocks + item * max_sel;
@@ -73,8 +99,7 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
   int pos = ns * nb;
 
   const int ncand = g.Fh - ns;
-  const float* frm = k_frm + (bh * g.Fh + ns) * D;
-  for (int c = lane; c < ncand; c += 64) fscore[c] = dot_f64<D>(qv, frm + (int64_t)c * D);
+  for (int c = lane; c < ncand; c += 64) fscore[c] = dot_f64<D>(qv, k_frm + key_row(FUSED, g, bh, ns + c) * D);
   __syncthreads();
   rank_keep(fscore, ncand, kf, fkeep, lane);
   __syncthreads();
@@ -85,7 +110,7 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
     const int f = ns + c;
     if (sel_frames != nullptr && lane == 0 && nf < kf_stride) sel_frames[item * kf_stride + nf] = f;
     ++nf;
-    const float* blk = k_blk + (bh * g.Fh + f) * (int64_t)nb * D;
+    const float* blk = k_blk + key_row(FUSED, g, bh, f) * (int64_t)nb * D;
     for (int j = lane; j < nb; j += 64) bscore[j] = dot_f64<D>(qv, blk + (int64_t)j * D);
     __syncthreads();
     rank_keep(bscore, nb, kb, bkeep, lane);
@@ -185,13 +210,46 @@ hipError_t launch_select(const KGeom& g, const float* q_blk, const float* k_blk,
                          int32_t kb, int32_t k_frames_stride, int32_t* sel_frames, int32_t* sel_blocks,
                          int32_t* n_sel, int32_t max_sel, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)g.B * g.H * g.nqb);
+  const float* no_q = nullptr;
   if (g.D == 128)
-    hipLaunchKernelGGL((select_kernel<128>), dim3(grid), dim3(64), 0, stream, q_blk, k_blk, k_frm, g, kf, kb,
-                       k_frames_stride, sel_frames, sel_blocks, n_sel, max_sel);
+    hipLaunchKernelGGL((select_kernel<128, false, float>), dim3(grid), dim3(64), 0, stream, q_blk, no_q, k_blk, k_frm,
+                       g, kf, kb, k_frames_stride, sel_frames, sel_blocks, n_sel, max_sel, nullptr);
   else
-    hipLaunchKernelGGL((select_kernel<64>), dim3(grid), dim3(64), 0, stream, q_blk, k_blk, k_frm, g, kf, kb,
-                       k_frames_stride, sel_frames, sel_blocks, n_sel, max_sel);
+    hipLaunchKernelGGL((select_kernel<64, false, float>), dim3(grid), dim3(64), 0, stream, q_blk, no_q, k_blk, k_frm,
+                       g, kf, kb, k_frames_stride, sel_frames, sel_blocks, n_sel, max_sel, nullptr);
   return hipGetLastError();
+}
+
+namespace {
+template <typename T, int D>
+hipError_t launch_fused_typed(const KGeom& g, const void* q, const float* kp_blk, const float* kp_frm, int32_t kf,
+                              int32_t kb, int32_t k_frames_stride, int32_t* sel_frames, int32_t* sel_blocks,
+                              int32_t* n_sel, int32_t max_sel, float* q_blk, hipStream_t stream) {
+  const unsigned grid = (unsigned)((int64_t)g.B * g.H * g.nqb);
+  const float* no_qblk = nullptr;
+  hipLaunchKernelGGL((select_kernel<D, true, T>), dim3(grid), dim3(64), 0, stream, no_qblk, static_cast<const T*>(q),
+                     kp_blk, kp_frm, g, kf, kb, k_frames_stride, sel_frames, sel_blocks, n_sel, max_sel, q_blk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_select_fused(const KGeom& g, int32_t dtype, const void* q, const float* kp_blk, const float* kp_frm,
+                               int32_t kf, int32_t kb, int32_t k_frames_stride, int32_t* sel_frames,
+                               int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, float* q_blk,
+                               hipStream_t stream) {
+  if (dtype == LF_BF16) {
+    if (g.D == 128)
+      return launch_fused_typed<__bf16, 128>(g, q, kp_blk, kp_frm, kf, kb, k_frames_stride, sel_frames, sel_blocks,
+                                             n_sel, max_sel, q_blk, stream);
+    return launch_fused_typed<__bf16, 64>(g, q, kp_blk, kp_frm, kf, kb, k_frames_stride, sel_frames, sel_blocks,
+                                          n_sel, max_sel, q_blk, stream);
+  }
+  if (g.D == 128)
+    return launch_fused_typed<float, 128>(g, q, kp_blk, kp_frm, kf, kb, k_frames_stride, sel_frames, sel_blocks,
+                                          n_sel, max_sel, q_blk, stream);
+  return launch_fused_typed<float, 64>(g, q, kp_blk, kp_frm, kf, kb, k_frames_stride, sel_frames, sel_blocks, n_sel,
+                                       max_sel, q_blk, stream);
 }
 
 hipError_t launch_select_blocks(const KGeom& g, const float* q_blk, const float* k_blk, int32_t k,

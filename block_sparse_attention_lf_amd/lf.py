@@ -28,7 +28,7 @@ STATUS = {0: "LF_OK", -1: "LF_ERR_NULL", -2: "LF_ERR_GEOM", -3: "LF_ERR_DTYPE", 
           -5: "LF_ERR_ALIGN", -6: "LF_ERR_HIP", -7: "LF_ERR_SLOT", -8: "LF_ERR_ARG"}
 
 # Every symbol include/lf.h declares.
-EXPORTS = ("lf_compress", "lf_max_sel", "lf_select", "lf_max_sel_1d", "lf_select_blocks", "lf_block_sparse_attn",
+EXPORTS = ("lf_compress", "lf_max_sel", "lf_select", "lf_max_sel_1d", "lf_select_blocks", "lf_pool_keys", "lf_select_fused", "lf_block_sparse_attn",
            "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error")
 
 
@@ -75,6 +75,9 @@ def lib() -> ctypes.CDLL:
         "lf_max_sel": (ctypes.c_int32, [G, ctypes.c_int32, ctypes.c_int32]),
         "lf_select": (ctypes.c_int, [G, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P]),
         "lf_max_sel_1d": (ctypes.c_int32, [G, ctypes.c_int32]),
+        "lf_pool_keys": (ctypes.c_int, [G, _P, _I32P, ctypes.c_int32, _P, _P, _P]),
+        "lf_select_fused": (ctypes.c_int, [G, _P, _P, _P, _I32P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                                           ctypes.c_int32, _P, _P]),
         "lf_select_blocks": (ctypes.c_int, [G, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P]),
         "lf_block_sparse_attn": (ctypes.c_int, [G, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32, ctypes.c_float,
                                                 _P, _P, _P]),
@@ -173,6 +176,38 @@ def lf_select(g: lf_geom, q_blk, k_blk, k_frm, k_frames: int, k_blocks: int, sel
         _need(sel_frames, (g.batch, g.heads, g.n_qblocks, k_frames), torch.int32, "sel_frames")
     _check(lib().lf_select(ctypes.byref(g), _ptr(q_blk), _ptr(k_blk), _ptr(k_frm), k_frames, k_blocks,
                            _ptr(sel_frames), _ptr(sel_blocks), _ptr(n_sel), max_sel, _stream(stream)), "lf_select")
+
+
+def lf_pool_keys(g: lf_geom, k_cache, slots, kp_blk, kp_frm, stream=None) -> None:
+    """Pool the frames in the given cache slots into slot-indexed pooled caches (see include/lf.h)."""
+    D, nb, S = g.head_dim, g.blocks_per_frame, g.cache_slots
+    _need(k_cache, (g.batch, g.heads, S, g.tokens_per_frame, D), _tdtype(g), "k_cache")
+    _need(kp_blk, (g.batch, g.heads, S, nb, D), torch.float32, "kp_blk")
+    _need(kp_frm, (g.batch, g.heads, S, D), torch.float32, "kp_frm")
+    arr = np.ascontiguousarray(np.asarray(slots, np.int32))
+    sp = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    _check(lib().lf_pool_keys(ctypes.byref(g), _ptr(k_cache), sp, int(arr.size), _ptr(kp_blk), _ptr(kp_frm),
+                              _stream(stream)), "lf_pool_keys")
+
+
+def lf_select_fused(g: lf_geom, q, kp_blk, kp_frm, frame_slot, k_frames: int, k_blocks: int, sel_frames, sel_blocks,
+                    n_sel, q_blk=None, stream=None) -> None:
+    """Query pooling + two-stage selection against slot-indexed pooled keys (see include/lf.h)."""
+    D, nb, S = g.head_dim, g.blocks_per_frame, g.cache_slots
+    _need(q, (g.batch, g.heads, g.q_len, D), _tdtype(g), "q")
+    _need(kp_blk, (g.batch, g.heads, S, nb, D), torch.float32, "kp_blk")
+    _need(kp_frm, (g.batch, g.heads, S, D), torch.float32, "kp_frm")
+    max_sel = sel_blocks.shape[-1]
+    _need(sel_blocks, (g.batch, g.heads, g.n_qblocks, max_sel), torch.int32, "sel_blocks")
+    _need(n_sel, (g.batch, g.heads, g.n_qblocks), torch.int32, "n_sel")
+    if sel_frames is not None:
+        _need(sel_frames, (g.batch, g.heads, g.n_qblocks, k_frames), torch.int32, "sel_frames")
+    if q_blk is not None:
+        _need(q_blk, (g.batch, g.heads, g.n_qblocks, D), torch.float32, "q_blk")
+    arr, sp = _slots(frame_slot)
+    _check(lib().lf_select_fused(ctypes.byref(g), _ptr(q), _ptr(kp_blk), _ptr(kp_frm), sp, k_frames, k_blocks,
+                                 _ptr(sel_frames), _ptr(sel_blocks), _ptr(n_sel), max_sel, _ptr(q_blk),
+                                 _stream(stream)), "lf_select_fused")
 
 
 def lf_max_sel_1d(g: lf_geom, k_total: int) -> int:

@@ -128,6 +128,30 @@ lf_status lf_select(const lf_geom* g, const float* q_blk, const float* k_blk, co
                     int32_t* n_sel, int32_t max_sel, lf_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * Pool-on-commit and the fused per-step selection ([LF-tech] 2.2; [SF]
+ * rolling cache: frames in the cache do not change until evicted, so their
+ * pooled keys are computed once, when the frame is committed).
+ *
+ * lf_pool_keys pools the frames held in cache slots slots[0 .. n_slots-1]
+ * (a HOST array of distinct slots in [0, cache_slots), n_slots <=
+ * LF_MAX_FRAMES) into caches indexed by slot, with lf_compress's numerics:
+ *   kp_blk [B, H, cache_slots, nb, D] float32   block means
+ *   kp_frm [B, H, cache_slots, D]     float32   frame means
+ * Other slots are left untouched. n_slots == 0 is a no-op.
+ *
+ * lf_select_fused does, per query block, lf_compress's query pooling and
+ * lf_select's two-stage selection in one launch, reading the pooled keys of
+ * logical frame f from slot frame_slot[f] of kp_blk / kp_frm. Its outputs
+ * equal lf_compress + lf_select on the same inputs bit for bit. q_blk
+ * (nullable) receives the pooled queries. Other arguments as lf_select.
+ * ------------------------------------------------------------------------- */
+lf_status lf_pool_keys(const lf_geom* g, const void* k_cache, const int32_t* slots, int32_t n_slots, float* kp_blk,
+                       float* kp_frm, lf_stream stream);
+lf_status lf_select_fused(const lf_geom* g, const void* q, const float* kp_blk, const float* kp_frm,
+                          const int32_t* frame_slot, int32_t k_frames, int32_t k_blocks, int32_t* sel_frames,
+                          int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, float* q_blk, lf_stream stream);
+
+/* ---------------------------------------------------------------------------
  * Single-level ("1D") selection, the ablation baseline ([LF-press] 4,
  * ablation paragraph: block sparse attention without the frame stage). Per
  * (batch, head, query block): block score <q_blk, k_blk[id]> in float64 for

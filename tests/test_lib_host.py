@@ -161,3 +161,22 @@ def test_select_blocks_validation():
     assert L.lf_select_blocks(ctypes.byref(g), None, p, 30, p, p, 30, None) == -1
     big = lf.geom_of(I.WAN480P_CHUNK.replace(hist_frames=200, cache_slots=203, block=16))
     assert L.lf_select_blocks(ctypes.byref(big), p, p, 30, p, p, 10 ** 6, None) == -2
+
+
+def test_pool_keys_validation():
+    w = I.WAN480P_CHUNK
+    g = lf.geom_of(w)
+    L = lf.lib()
+    p = ctypes.c_void_p(4096)
+
+    def call(slots, n=None):
+        arr = np.asarray(slots, np.int32)
+        return L.lf_pool_keys(ctypes.byref(g), p, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                              len(slots) if n is None else n, p, p, None)
+
+    assert call([0, 1], n=0) == 0          # no-op
+    assert call([0, w.cache_slots]) == -7  # slot out of range
+    assert call([3, 3]) == -7              # slot named twice
+    assert call([0], n=-1) == -8
+    assert call([0], n=lf.LF_MAX_FRAMES + 1) == -8
+    assert L.lf_pool_keys(ctypes.byref(g), None, None, 1, p, p, None) == -1
