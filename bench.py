@@ -16,6 +16,7 @@ step (FLOPs actually needed on the selected blocks plus the current chunk,
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -42,6 +43,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the 480p chunk)")
+    ap.add_argument("--path", choices=("step", "fused"), default="step",
+                    help="step: compress + select + attention every step (every hot-path row); fused: keys pooled "
+                         "once on commit, then fused query pooling + selection and attention per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-qblocks", type=int, default=0, help="0: every query block (the whole call)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -183,16 +187,51 @@ def main():
         torch.cuda.synchronize()
         flops.append(effective_flops(w, bufs.sel_blocks.cpu().numpy(), bufs.n_sel.cpu().numpy()))
 
+    # Fused path: the pooled keys of every history frame live in a slot-indexed
+    # cache, filled when the frame is committed (once per frame, not per step).
+    pooled = []
+    commit_ms = None
+    if args.path == "fused":
+        S, nb, d = w.cache_slots, w.blocks_per_frame, w.head_dim
+        hist_slots = [int(x) for x in slots[:w.hist_frames]]
+        for q, kc, vc in sets:
+            kp = (torch.empty((w.batch, w.heads, S, nb, d), dtype=torch.float32, device="cuda"),
+                  torch.empty((w.batch, w.heads, S, d), dtype=torch.float32, device="cuda"))
+            lf.lf_pool_keys(g, kc, hist_slots, kp[0], kp[1], stream)
+            pooled.append(kp)
+        # cost of one commit: pooling the chunk's own frames (they become history)
+        chunk_slots = [int(x) for x in slots[w.hist_frames:w.hist_frames + w.chunk_frames]]
+        cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        times = []
+        for r in range(6):
+            kc = sets[r % N_SETS][1]
+            cev[0].record(stream)
+            lf.lf_pool_keys(g, kc, chunk_slots, pooled[r % N_SETS][0], pooled[r % N_SETS][1], stream)
+            cev[1].record(stream)
+            torch.cuda.synchronize()
+            times.append(cev[0].elapsed_time(cev[1]))
+        commit_ms = float(np.median(times[1:]))
+        for (q, kc, vc), kp in zip(sets, pooled):  # restore the history pooling the steps read
+            lf.lf_pool_keys(g, kc, hist_slots, kp[0], kp[1], stream)
+        torch.cuda.synchronize()
+
     def step(i, ev=None):
         q, kc, vc = sets[i % N_SETS]
         sl = host_side()
         if ev is not None:
             ev[0].record(stream)
-        lf.lf_compress(g, q, kc, sl, bufs.q_blk, bufs.k_blk, bufs.k_frm, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        lf.lf_select(g, bufs.q_blk, bufs.k_blk, bufs.k_frm, w.k_frames, w.k_blocks, bufs.sel_frames,
-                     bufs.sel_blocks, bufs.n_sel, stream)
+        if args.path == "fused":
+            kp_blk, kp_frm = pooled[i % N_SETS]
+            if ev is not None:
+                ev[1].record(stream)
+            lf.lf_select_fused(g, q, kp_blk, kp_frm, sl, w.k_frames, w.k_blocks, bufs.sel_frames, bufs.sel_blocks,
+                               bufs.n_sel, None, stream)
+        else:
+            lf.lf_compress(g, q, kc, sl, bufs.q_blk, bufs.k_blk, bufs.k_frm, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            lf.lf_select(g, bufs.q_blk, bufs.k_blk, bufs.k_frm, w.k_frames, w.k_blocks, bufs.sel_frames,
+                         bufs.sel_blocks, bufs.n_sel, stream)
         if ev is not None:
             ev[2].record(stream)
         lf.lf_block_sparse_attn(g, q, kc, vc, sl, bufs.sel_blocks, bufs.n_sel, scale, bufs.out, None, stream)
@@ -204,14 +243,20 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` steps between two device synchronisations.
+    # The cyclic garbage collector is paused inside it: a full pass over a
+    # process holding torch takes tens of milliseconds and would land in a
+    # random step.
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         step(i, evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
 
     ms_step = (t1 - t0) * 1e3 / K
     comp = [e[0].elapsed_time(e[1]) for e in evs]
@@ -234,7 +279,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "tokens_per_frame": w.tokens_per_frame, "block": w.block, "chunk_frames": w.chunk_frames,
                    "hist_frames": w.hist_frames, "k_frames": w.k_frames, "k_blocks": w.k_blocks,
-                   "sparsity": w.sparsity, "input_sets_rotated": N_SETS,
+                   "sparsity": w.sparsity, "input_sets_rotated": N_SETS, "path": args.path,
                    "bytes_per_input_set": int(set_bytes)},
         "roofline": {"bound": "mfma", "kernel": "attn_kernel (lf_block_sparse_attn)",
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
@@ -247,6 +292,11 @@ def main():
                      "algorithmic_bytes": cbytes},
         "attention_pct_of_mfma_peak": round(100 * attn_tflops / peak, 2),
     }
+    if args.path == "fused":
+        # one stage: query pooling + selection; history pooling is paid on commit
+        result["stages_ms"] = {"select_fused": round(float(np.mean(sel)), 4), "attention": round(attn_ms, 4)}
+        result.pop("compress")
+        result["pool_on_commit"] = {"ms_per_commit": round(commit_ms, 4), "frames_per_commit": w.chunk_frames}
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 2
         src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
