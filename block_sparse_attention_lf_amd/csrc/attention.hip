@@ -39,6 +39,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -278,6 +279,19 @@ struct Walk {
       b1[e] = (__bf16)p[8 + e];
     }
   }
+  // Sum of the 16 bf16 probabilities (two dot products with (1, 1) per pair
+  // of registers): the normaliser adds exactly the rounded values the PV
+  // MFMA multiplies.
+  static __device__ __forceinline__ float psum(const bf16x8& b0, const bf16x8& b1) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float a = 0.0f, c = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{b0[2 * i], b0[2 * i + 1]}, one, a, false);
+      c = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{b1[2 * i], b1[2 * i + 1]}, one, c, false);
+    }
+    return a + c;
+  }
   // The exact path for one half, taken when the fast path's probabilities
   // could be too large (or the walk has no reference yet): recompute the
   // half's scores, move the reference to the true running max (both lanes of
@@ -314,7 +328,7 @@ struct Walk {
       s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mc));
       ps += s[r];
     }
-    return ps;
+    return ps;  // (the bf16 path re-sums after rounding; the fp32 path uses this)
   }
 
   // One bf16 tile. Online softmax without a per-tile max: probabilities are
@@ -363,7 +377,6 @@ struct Walk {
       for (int u = 0; u < 16 / QSTEPS; ++u) {
         const int r = t * (16 / QSTEPS) + u;
         s0[r] = pin(__builtin_amdgcn_exp2f(fmaf(s0[r], c2, -mc)));
-        ps0 += s0[r];
       }
       if (t >= QSTEPS - DB) va[t - (QSTEPS - DB)] = load_v1(vs, 0, t - (QSTEPS - DB));
       if (t & 1) issue_one<true>(nx, t / 2);
@@ -371,10 +384,15 @@ struct Walk {
     }
 #pragma unroll
     for (int i = QSTEPS / 2; i < LI; ++i) issue_one<true>(nx, i);
-    if (__builtin_amdgcn_ballot_w64(!(ps0 <= kFastLimit)) != 0) ps0 = exact_half(ks, 0, count, s0);
-    l_run += ps0;
     bf16x8 b0, b1;
     to_bf16(s0, b0, b1);
+    ps0 = psum(b0, b1);
+    if (__builtin_amdgcn_ballot_w64(!(ps0 <= kFastLimit)) != 0) {
+      exact_half(ks, 0, count, s0);
+      to_bf16(s0, b0, b1);
+      ps0 = psum(b0, b1);
+    }
+    l_run += ps0;
     if (count < BN) mask_half(s1, 1, count);
     LF_FENCE;
     // C: O^T += V[0:32]^T P0^T with the softmax of S1 between its MFMAs. V
@@ -392,13 +410,17 @@ struct Walk {
       for (int u = 0; u < 16 / (2 * DB); ++u) {
         const int r = j * (16 / (2 * DB)) + u;
         s1[r] = pin(__builtin_amdgcn_exp2f(fmaf(s1[r], c2, -mc)));
-        ps1 += s1[r];
       }
       LF_FENCE;
     }
-    if (__builtin_amdgcn_ballot_w64(!(ps1 <= kFastLimit)) != 0) ps1 = exact_half(ks, 1, count, s1);
-    l_run += ps1;
     to_bf16(s1, b0, b1);
+    ps1 = psum(b0, b1);
+    if (__builtin_amdgcn_ballot_w64(!(ps1 <= kFastLimit)) != 0) {
+      exact_half(ks, 1, count, s1);
+      to_bf16(s1, b0, b1);
+      ps1 = psum(b0, b1);
+    }
+    l_run += ps1;
     LF_FENCE;
     // D: O^T += V[32:64]^T P1^T.
 #pragma unroll
