@@ -47,6 +47,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int BN = 64;     // keys per tile
+// bf16 blocks of 33..64 keys use the single-stage kernel (one query block
+// per workgroup) instead of the double-buffered one.
+constexpr bool kSingleStage = true;
 
 template <typename T>
 struct Mma;
@@ -107,11 +110,11 @@ constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
 // One workgroup's walk: per-wavefront query fragments and accumulators, the
 // scalar tile producer, the LDS loader and the per-tile math.
-template <typename T, int D, int WPQ>
+template <typename T, int D, int WPQ, int QPWT = 4 / WPQ>
 struct Walk {
   using M = Mma<T>;
   using frag = typename M::frag;
-  static constexpr int QPW = 4 / WPQ;              // query blocks per workgroup
+  static constexpr int QPW = QPWT;                 // query blocks per workgroup
   static constexpr int NW = WPQ * QPW;             // wavefronts
   static constexpr int NT = 64 * NW;
   static constexpr int ES = (int)sizeof(T);
@@ -148,6 +151,16 @@ struct Walk {
   const uint2* walk;  // LDS table of history tiles, see the kernel
   int tpf, n_cur, n_tiles, all_mask, t_next, cf, ct;
   int64_t frame_elems, bh_base, cur_base;
+
+  // A tile descriptor of the walk.
+  struct Desc {
+    int64_t off;
+    int count, mask;
+    bool have;
+  };
+  // Advances d to the next tile; at the end of the walk d keeps its tile
+  // and d.have turns false.
+  __device__ __forceinline__ void advance(Desc& d) { d.have = produce(d.off, d.count, d.mask); }
 
   // Fills (off, count, mask) of the next tile: the current chunk's tiles in
   // order (counters, no divisions), then the history tiles of the table;
@@ -234,6 +247,11 @@ struct Walk {
 #endif
     }
   }
+  template <bool V>
+  __device__ __forceinline__ void issue_all(const Next& n) const {
+#pragma unroll
+    for (int i = 0; i < LI; ++i) issue_one<V>(n, i);
+  }
   __device__ __forceinline__ void issue(const Next& n) const {
 #pragma unroll
     for (int i = 0; i < LI; ++i) {
@@ -309,6 +327,10 @@ struct Walk {
     }
     __builtin_amdgcn_sched_barrier(0);
     if (count < (kh + 1) * 32) mask_half(s, kh, count);
+    return exact_from_scores(s);
+  }
+  // The exact path from a half's masked raw scores (in s; probabilities out).
+  __device__ __forceinline__ float exact_from_scores(f32x16& s) {
     float mt = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
@@ -433,6 +455,102 @@ struct Walk {
 #undef LF_FENCE
   }
 
+  // ---- single-stage tile (one K and one V buffer per workgroup) ----------
+  // Phase 1 reads only the K tile: S0, then S1 with the softmax of S0
+  // between its MFMAs; this tile's V DMA goes out meanwhile (the V buffer was
+  // freed by the barrier before). Leaves P0 in b0/b1 and the raw S1.
+  __device__ __forceinline__ void ss_phase1(const char* ks, int count, const Next& nv, f32x16& s1, bf16x8& b0,
+                                            bf16x8& b1) {
+#define LF_FENCE __builtin_amdgcn_sched_barrier(0)
+    frag kf[QSTEPS];
+    f32x16 s0;
+    load_k(ks, 0, kf);
+    LF_FENCE;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) {
+      s0 = M::mfma(kf[t], qf[t], s0);
+      kf[t] = load_k1(ks, 1, t);
+      issue_one<true>(nv, t);
+      LF_FENCE;
+    }
+#pragma unroll
+    for (int i = QSTEPS; i < LI; ++i) issue_one<true>(nv, i);
+    if (count < 32) mask_half(s0, 0, count);
+    LF_FENCE;
+    const float mc = m_run * c2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s1[r] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) {
+      s1 = M::mfma(kf[t], qf[t], s1);
+      LF_FENCE;
+#pragma unroll
+      for (int u = 0; u < 16 / QSTEPS; ++u) {
+        const int r = t * (16 / QSTEPS) + u;
+        s0[r] = pin(__builtin_amdgcn_exp2f(fmaf(s0[r], c2, -mc)));
+      }
+      LF_FENCE;
+    }
+    to_bf16(s0, b0, b1);
+    float ps0 = psum(b0, b1);
+    if (__builtin_amdgcn_ballot_w64(!(ps0 <= kFastLimit)) != 0) {
+      exact_half(ks, 0, count, s0);
+      to_bf16(s0, b0, b1);
+      ps0 = psum(b0, b1);
+    }
+    l_run += ps0;
+    if (count < BN) mask_half(s1, 1, count);
+#undef LF_FENCE
+  }
+  // Phase 2 reads only the V tile (the next tile's K DMA goes out
+  // meanwhile, so the rare exact path of S1 works from the saved raw
+  // scores, not from K): PV0 with the softmax of S1 between its MFMAs, then
+  // PV1.
+  __device__ __forceinline__ void ss_phase2(const char* vs, const Next& nk, f32x16& s1, bf16x8& b0, bf16x8& b1) {
+#define LF_FENCE __builtin_amdgcn_sched_barrier(0)
+    bf16x8 va[DB];
+    const f32x16 s1raw = s1;
+    load_v(vs, 0, va);
+    LF_FENCE;
+    const float mc = m_run * c2;
+#pragma unroll
+    for (int j = 0; j < 2 * DB; ++j) {
+      const int ps = j / DB, db = j % DB;
+      o[db] = M::mfma(va[db], ps == 0 ? b0 : b1, o[db]);
+      va[db] = load_v1(vs, ps + 1, db);
+      issue_one<false>(nk, j);
+      LF_FENCE;
+#pragma unroll
+      for (int u = 0; u < 16 / (2 * DB); ++u) {
+        const int r = j * (16 / (2 * DB)) + u;
+        s1[r] = pin(__builtin_amdgcn_exp2f(fmaf(s1[r], c2, -mc)));
+      }
+      LF_FENCE;
+    }
+#pragma unroll
+    for (int i = 2 * DB; i < LI; ++i) issue_one<false>(nk, i);
+    to_bf16(s1, b0, b1);
+    float ps1 = psum(b0, b1);
+    if (__builtin_amdgcn_ballot_w64(!(ps1 <= kFastLimit)) != 0) {
+      s1 = s1raw;
+      exact_from_scores(s1);
+      to_bf16(s1, b0, b1);
+      ps1 = psum(b0, b1);
+    }
+    l_run += ps1;
+    LF_FENCE;
+#pragma unroll
+    for (int j = 0; j < 2 * DB; ++j) {
+      const int ps = 2 + j / DB, db = j % DB;
+      o[db] = M::mfma(va[db], ps == 2 ? b0 : b1, o[db]);
+      if (ps == 2) va[db] = load_v1(vs, 3, db);
+      LF_FENCE;
+    }
+#undef LF_FENCE
+  }
+
   __device__ __forceinline__ void compute(const char* ks, const char* vs, int count, const Next& nx) {
     if constexpr (ES == 2) {
       compute_bf16(ks, vs, count, nx);
@@ -493,12 +611,18 @@ struct Walk {
   }
 };
 
-template <typename T, int D, int WPQ>
-__global__ __launch_bounds__(64 * WPQ * (4 / WPQ), (WAVES_PER_SIMD<T, WPQ>)) void attn_kernel(
+// SS = false: a workgroup owns 4/WPQ query blocks (128 rows) and
+// double-buffers K/V tiles (one barrier per tile). SS = true (bf16): a
+// workgroup owns one query block, holds one K and one V tile (40 KB of LDS
+// at b = 64, so four workgroups share a CU) and alternates them around two
+// barriers per tile: V of tile t streams in while tile t's scores are formed,
+// K of tile t+1 while its PV products run.
+template <typename T, int D, int WPQ, bool SS>
+__global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T, WPQ>)) void attn_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ nsel, int max_sel, float scale, const KGeom g, T* __restrict__ out,
     float* __restrict__ lse) {
-  using W = Walk<T, D, WPQ>;
+  using W = Walk<T, D, WPQ, SS ? 1 : 4 / WPQ>;
   constexpr int QPW = W::QPW, ES = W::ES, QSTEPS = W::QSTEPS, DB = W::DB;
 
   // Two named stage buffers (not one indexed array): the loop below is
@@ -507,8 +631,6 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), (WAVES_PER_SIMD<T, WPQ>)) voi
   // is filling the other.
   __shared__ __attribute__((aligned(1024))) char k0[W::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v0[W::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char k1[W::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v1[W::TILE_BYTES];
   // History tiles of the walk, one entry each (see below); a block of more
   // than BN keys is two tiles.
   constexpr int WALK_CAP = QPW * LF_MAX_SEL * (WPQ > 2 ? 2 : 1);
@@ -660,6 +782,45 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), (WAVES_PER_SIMD<T, WPQ>)) voi
   w.l_run = 0.0f;
   w.c2 = scale * kLog2e;
 
+  if constexpr (SS) {
+    // Single-stage walk. K of the first tile is loaded up front; then per
+    // tile: phase 1 on K (this tile's V DMA in flight), barrier, phase 2 on V
+    // (next tile's K DMA in flight), barrier. At the end of the walk the
+    // last tile's K is re-read into the buffer nobody reads any more.
+    int64_t c_off = 0;
+    int c_cnt = 0, c_msk = 0;
+    w.produce(c_off, c_cnt, c_msk);  // the current chunk always has a tile
+    w.template issue_all<false>(w.next_tile(k0, v0, c_off, c_cnt));
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    for (;;) {
+      const typename W::Next nv = w.next_tile(k0, v0, c_off, c_cnt);
+      f32x16 s1;
+      bf16x8 b0, b1;
+      if (w.wave_active)
+        w.ss_phase1(k0, c_cnt, nv, s1, b0, b1);
+      else
+        w.template issue_all<true>(nv);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this tile's V has landed (own share)
+      __syncthreads();                       // ... everyone's, and nobody reads K any more
+      int64_t n_off = c_off;
+      int n_cnt = c_cnt, n_msk = c_msk;
+      const bool more = w.produce(n_off, n_cnt, n_msk);
+      const typename W::Next nk = w.next_tile(k0, v0, n_off, n_cnt);
+      if (w.wave_active)
+        w.ss_phase2(v0, nk, s1, b0, b1);
+      else
+        w.template issue_all<false>(nk);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // next tile's K has landed (own share)
+      __syncthreads();                       // ... everyone's, and nobody reads V any more
+      if (!more) break;
+      c_off = n_off;
+      c_cnt = n_cnt;
+      c_msk = n_msk;
+    }
+  } else {
+  __shared__ __attribute__((aligned(1024))) char k1[W::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1[W::TILE_BYTES];
   // Double-buffered walk, unrolled by two so each half names its buffers.
   int64_t noff = 0;
   int ncount = 0, nmask = 0;
@@ -691,6 +852,8 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), (WAVES_PER_SIMD<T, WPQ>)) voi
     }
   }
 
+  }
+
   // No load may still be writing LDS when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   if (!w.wave_active || w.qr >= w.nrows) return;
@@ -715,12 +878,12 @@ __global__ __launch_bounds__(64 * WPQ * (4 / WPQ), (WAVES_PER_SIMD<T, WPQ>)) voi
   if (lse != nullptr && w.h == 0) lse[w.bh * g.Lq + w.qrow0 + w.qr] = w.m_run * scale + logf(l_tot);
 }
 
-template <typename T, int D, int WPQ>
+template <typename T, int D, int WPQ, bool SS = false>
 hipError_t launch_typed(const KGeom& g, const void* q, const void* k, const void* v, const int32_t* sel,
                         const int32_t* nsel, int max_sel, float scale, void* out, float* lse, hipStream_t stream) {
-  constexpr int QPW = 4 / WPQ;
+  constexpr int QPW = SS ? 1 : 4 / WPQ;
   const unsigned grid = (unsigned)((int64_t)g.B * g.H * ((g.nqb + QPW - 1) / QPW));
-  hipLaunchKernelGGL((attn_kernel<T, D, WPQ>), dim3(grid), dim3(64 * WPQ * QPW), 0, stream,
+  hipLaunchKernelGGL((attn_kernel<T, D, WPQ, SS>), dim3(grid), dim3(64 * WPQ * QPW), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sel, nsel, max_sel,
                      scale, g, static_cast<T*>(out), lse);
   return hipGetLastError();
@@ -731,7 +894,11 @@ hipError_t launch_d(const KGeom& g, const void* q, const void* k, const void* v,
                     const int32_t* nsel, int max_sel, float scale, void* out, float* lse, hipStream_t stream) {
   switch ((g.b + 31) / 32) {
     case 1: return launch_typed<T, D, 1>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
-    case 2: return launch_typed<T, D, 2>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
+    case 2:
+      if constexpr (sizeof(T) == 2) {
+        if (kSingleStage) return launch_typed<T, D, 2, true>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
+      }
+      return launch_typed<T, D, 2>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
     case 3: return launch_typed<T, D, 3>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
     default: return launch_typed<T, D, 4>(g, q, k, v, sel, nsel, max_sel, scale, out, lse, stream);
   }

@@ -18,7 +18,11 @@ from block_sparse_attention_lf_amd import lf
 from oracle import lf_oracle as O
 
 TIE_REL = 1e-5
-MAX_ABS, MEAN_ABS, REL_L2, LSE_ABS = 2e-2, 2e-3, 1e-2, 2e-3
+MAX_ABS, MEAN_ABS, REL_L2 = 2e-2, 2e-3, 1e-2
+# The kernel's softmax normaliser is the sum of the probabilities it feeds the
+# P.V product, i.e. rounded to bf16 (relative error at most 2^-8 each), so its
+# log can be off by up to ln(1 + 2^-8) = 3.9e-3 when one term dominates.
+LSE_ABS = 4e-3
 
 
 def to_dev(x: np.ndarray, dtype: str) -> torch.Tensor:

@@ -27,7 +27,7 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _full_check(w, x=None, k_frames=None, k_blocks=None, all_rows=False, n_random=4):
+def _full_check(w, x=None, k_frames=None, k_blocks=None, all_rows=False, n_random=4, scale_mult=1.0):
     k_frames = w.k_frames if k_frames is None else k_frames
     k_blocks = w.k_blocks if k_blocks is None else k_blocks
     _say(f"[parity] {w.name} B={w.batch} H={w.heads} d={w.head_dim} T={w.tokens_per_frame} b={w.block} "
@@ -38,7 +38,7 @@ def _full_check(w, x=None, k_frames=None, k_blocks=None, all_rows=False, n_rando
     P.assert_pooled_bit_exact(bufs, c)
     n, excused, bad = P.compare_selection(w, bufs, s, k_frames, k_blocks)
     assert not bad, f"{len(bad)} of {n} selections differ without a tie, first: {bad[0]}"
-    scale = 1.0 / math.sqrt(w.head_dim)
+    scale = scale_mult / math.sqrt(w.head_dim)
     qbs = ([(b, h, qb) for b in range(w.batch) for h in range(w.heads) for qb in range(w.n_qblocks)]
            if all_rows else P.sample_qblocks(w, n_random))
     out, lse = P.gpu_attention(w, g, dev, x, s["sel_blocks"], s["n_sel"], scale)
@@ -122,6 +122,19 @@ def test_odd_geometries(dtype, d, T, b):
                    chunk_frames=2, hist_frames=5, n_sink=1, cache_slots=8, dtype=dtype, k_frames=2, k_blocks=2,
                    sparsity=float("nan"), seed=5, dist="normal", chunk_index=4)
     _full_check(w, all_rows=True)
+
+
+@pytest.mark.parametrize("dtype,b,mult", [("bf16", 64, 4.0), ("bf16", 64, 16.0), ("bf16", 128, 16.0),
+                                          ("f32", 64, 16.0)])
+def test_sharp_logits(dtype, b, mult):
+    """Logits of std `mult` (unit-normal q and k, scale mult/sqrt(d)). At std 16 the maximum over the
+    whole key set sits some 20 above the maximum of the first tile, so the running maximum is overtaken
+    by more than 2^16 in probability and the kernel must take its exact rescaling branch, in both the
+    single-tile-buffered (b=64, bf16) and the double-buffered kernels."""
+    w = I.Workload(name=f"sharp_{dtype}_{b}_{mult:g}", batch=1, heads=4, head_dim=128, grid=(6, 20), block=b,
+                   chunk_frames=3, hist_frames=9, n_sink=1, cache_slots=12, dtype=dtype, k_frames=4, k_blocks=2,
+                   sparsity=float("nan"), seed=21, dist="normal", chunk_index=3)
+    _full_check(w, all_rows=True, scale_mult=mult)
 
 
 def test_dense_selection_equals_full_attention():
