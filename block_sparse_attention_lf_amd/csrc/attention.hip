@@ -329,6 +329,16 @@ struct Walk {
     if (count < (kh + 1) * 32) mask_half(s, kh, count);
     return exact_from_scores(s);
   }
+  // O *= alpha in place. Each multiply is a tied asm operand so the scaled
+  // accumulators keep their registers: with a plain multiply the register
+  // allocator may put the result elsewhere and then copy all of O back on the
+  // common path, where the rescale branch is not taken.
+  __device__ __forceinline__ void rescale_o(float alpha) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+  }
   // The exact path from a half's masked raw scores (in s; probabilities out).
   __device__ __forceinline__ float exact_from_scores(f32x16& s) {
     float mt = s[0];
@@ -339,10 +349,7 @@ struct Walk {
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
     l_run *= alpha;
     m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    rescale_o(alpha);
     const float mc = m_run * c2;
     float ps = 0.0f;
 #pragma unroll
@@ -586,10 +593,7 @@ struct Walk {
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
     l_run *= alpha;
     m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    rescale_o(alpha);
     const float mc = m_run * c2;
     float psum = 0.0f;
 #pragma unroll
@@ -787,6 +791,11 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
     // tile: phase 1 on K (this tile's V DMA in flight), barrier, phase 2 on V
     // (next tile's K DMA in flight), barrier. At the end of the walk the
     // last tile's K is re-read into the buffer nobody reads any more.
+    // Every wavefront runs both phases: each tile belongs to the one query
+    // block, and a wavefront past the block's last row holds zero query
+    // fragments (finite scores, discarded) and stores nothing. Skipping the
+    // math there would branch around O and cost register copies of O on
+    // every tile.
     int64_t c_off = 0;
     int c_cnt = 0, c_msk = 0;
     w.produce(c_off, c_cnt, c_msk);  // the current chunk always has a tile
@@ -797,20 +806,14 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
       const typename W::Next nv = w.next_tile(k0, v0, c_off, c_cnt);
       f32x16 s1;
       bf16x8 b0, b1;
-      if (w.wave_active)
-        w.ss_phase1(k0, c_cnt, nv, s1, b0, b1);
-      else
-        w.template issue_all<true>(nv);
+      w.ss_phase1(k0, c_cnt, nv, s1, b0, b1);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this tile's V has landed (own share)
       __syncthreads();                       // ... everyone's, and nobody reads K any more
       int64_t n_off = c_off;
       int n_cnt = c_cnt, n_msk = c_msk;
       const bool more = w.produce(n_off, n_cnt, n_msk);
       const typename W::Next nk = w.next_tile(k0, v0, n_off, n_cnt);
-      if (w.wave_active)
-        w.ss_phase2(v0, nk, s1, b0, b1);
-      else
-        w.template issue_all<false>(nk);
+      w.ss_phase2(v0, nk, s1, b0, b1);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);  // next tile's K has landed (own share)
       __syncthreads();                       // ... everyone's, and nobody reads V any more
       if (!more) break;
@@ -822,6 +825,9 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
   __shared__ __attribute__((aligned(1024))) char k1[W::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v1[W::TILE_BYTES];
   // Double-buffered walk, unrolled by two so each half names its buffers.
+  // A wavefront computes a tile only if its query block selected it; with a
+  // single query block per workgroup that holds for every tile (see the
+  // single-stage walk for the rows past the block's end).
   int64_t noff = 0;
   int ncount = 0, nmask = 0;
   bool have = w.produce(noff, ncount, nmask);
@@ -833,7 +839,7 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
       __syncthreads();                       // ... everyone's, and the other buffer is free
       have = w.produce(noff, ncount, nmask);
       const typename W::Next nx = w.next_tile(k1, v1, noff, ncount);
-      if (w.wave_active && ((mask >> w.lq) & 1))
+      if (W::QPW == 1 || (w.wave_active && ((mask >> w.lq) & 1)))
         w.compute(k0, v0, count, nx);
       else
         w.issue(nx);
@@ -845,7 +851,7 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
       __syncthreads();
       have = w.produce(noff, ncount, nmask);
       const typename W::Next nx = w.next_tile(k0, v0, noff, ncount);
-      if (w.wave_active && ((mask >> w.lq) & 1))
+      if (W::QPW == 1 || (w.wave_active && ((mask >> w.lq) & 1)))
         w.compute(k1, v1, count, nx);
       else
         w.issue(nx);
