@@ -6,17 +6,23 @@
 // sink frames are attended in full. Output: ascending logical block ids.
 //
 // Numerics: scores are float64 dot products of the float32 pooled vectors
-// (every product is exact in float64), accumulated in ascending d. A
-// candidate is kept when fewer than k others rank above it, where c ranks
-// above c' if its score is larger, or equal with a lower index. That is
-// exactly "stable sort descending, take the first k" without sorting.
+// (every product is exact in float64). The two-stage selection sums each dot
+// product as 8 partial sums over consecutive ranges of d (each ascending),
+// combined by a pairwise butterfly that leaves the same bits in all 8 lanes;
+// the single-level selection sums in ascending d. A candidate is kept when
+// fewer than k others rank above it, where c ranks above c' if its score is
+// larger, or equal with a lower index. That is exactly "stable sort
+// descending, take the first k" without sorting.
 //
-// Design: one wavefront per (batch, head, query block). Candidates map onto
-// lanes; each lane computes whole dot products (the pooled query is broadcast
-// from LDS), ranks are counted against the scores kept in LDS, and the kept
-// ids are compacted in ascending order with a ballot and a prefix popcount.
-// The whole step reads O(kf*nb + Fh) pooled vectors per query block,
-// independent of how long the history is beyond that.
+// Design: one wavefront per (batch, head, query block). Each dot product is
+// shared by 8 lanes (the pooled query is broadcast from LDS), so a wavefront
+// scores 8 candidates per round with dependent chains of D/8 fused
+// multiply-adds. The frame candidates are scored, ranked against the scores
+// kept in LDS, and then the blocks of all kept frames are scored as one batch
+// (up to 1024 at a time) and ranked inside their frame; kept ids are
+// compacted in ascending order with a ballot and a prefix popcount. The whole
+// step reads O(kf*nb + Fh) pooled vectors per query block, independent of how
+// long the history is beyond that.
 #include "pool.h"
 
 namespace lf {
@@ -33,6 +39,38 @@ __device__ inline double dot_f64(const float* __restrict__ qv_lds, const float* 
     acc = fma((double)qv_lds[d + 2], (double)kv.z, acc);
     acc = fma((double)qv_lds[d + 3], (double)kv.w, acc);
   }
+  return acc;
+}
+
+// Lanes sharing one dot product, candidates per wavefront round, and the
+// number of block candidates scored per batch.
+constexpr int kDotLanes = 8;
+constexpr int kPerRound = 64 / kDotLanes;
+constexpr int kBlockBatch = 1024;
+static_assert(LF_MAX_BLOCKS_PER_FRAME <= kBlockBatch, "one frame's blocks must fit a batch");
+
+// Dot product of the pooled query (LDS) with key row k, shared by the
+// kDotLanes lanes of one candidate: lane `part` sums d in [part*D/8,
+// (part+1)*D/8) in ascending order, then a butterfly adds the partial sums.
+// Every lane of the group returns the same value (a + b == b + a exactly).
+// All 64 lanes must call it (the butterfly exchanges across lanes).
+template <int D>
+__device__ inline double dot_split(const float* __restrict__ qv_lds, const float* __restrict__ k, int part) {
+  constexpr int SPAN = D / kDotLanes;
+  static_assert(SPAN % 4 == 0, "each lane reads whole float4s");
+  const float* kp = k + part * SPAN;
+  const float* qp = qv_lds + part * SPAN;
+  double acc = 0.0;
+#pragma unroll
+  for (int d = 0; d < SPAN; d += 4) {
+    const float4 kv = *reinterpret_cast<const float4*>(kp + d);
+    acc = fma((double)qp[d], (double)kv.x, acc);
+    acc = fma((double)qp[d + 1], (double)kv.y, acc);
+    acc = fma((double)qp[d + 2], (double)kv.z, acc);
+    acc = fma((double)qp[d + 3], (double)kv.w, acc);
+  }
+#pragma unroll
+  for (int m = 1; m < kDotLanes; m <<= 1) acc += __shfl_xor(acc, m);
   return acc;
 }
 
@@ -67,13 +105,15 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
                                                     int32_t* __restrict__ sel_frames,
                                                     int32_t* __restrict__ sel_blocks, int32_t* __restrict__ n_sel,
                                                     int max_sel, float* __restrict__ q_blk_out) {
-  __shared__ float qv[D];
+  __shared__ __attribute__((aligned(16))) float qv[D];
   __shared__ double fscore[LF_MAX_FRAMES];
   __shared__ unsigned char fkeep[LF_MAX_FRAMES];
-  __shared__ double bscore[LF_MAX_BLOCKS_PER_FRAME];
-  __shared__ unsigned char bkeep[LF_MAX_BLOCKS_PER_FRAME];
+  __shared__ double bscore[kBlockBatch];
+  __shared__ unsigned char bkeep[kBlockBatch];
+  __shared__ int bframe[LF_MAX_FRAMES];
 
   const int lane = threadIdx.x;
+  const int part = lane % kDotLanes, sub = lane / kDotLanes;
   const int64_t item = blockIdx.x;  // (b*H + h)*nqb + qb
   const int64_t bh = item / g.nqb;
   const int nb = g.nb, ns = g.ns;
@@ -98,32 +138,67 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
   for (int i = lane; i < ns * nb; i += 64) out[i] = i;  // sink frames in full
   int pos = ns * nb;
 
+  // Stage 1: frame scores (kPerRound candidates per round; lanes past the
+  // last candidate recompute the last one and drop it).
   const int ncand = g.Fh - ns;
-  for (int c = lane; c < ncand; c += 64) fscore[c] = dot_f64<D>(qv, k_frm + key_row(FUSED, g, bh, ns + c) * D);
+  for (int r0 = 0; r0 < ncand; r0 += kPerRound) {
+    const int c = r0 + sub;
+    const double sc = dot_split<D>(qv, k_frm + key_row(FUSED, g, bh, ns + min(c, ncand - 1)) * D, part);
+    if (c < ncand && part == 0) fscore[c] = sc;
+  }
   __syncthreads();
   rank_keep(fscore, ncand, kf, fkeep, lane);
   __syncthreads();
 
-  int nf = 0;
-  for (int c = 0; c < ncand; ++c) {
-    if (!fkeep[c]) continue;  // same value in every lane
-    const int f = ns + c;
-    if (sel_frames != nullptr && lane == 0 && nf < kf_stride) sel_frames[item * kf_stride + nf] = f;
-    ++nf;
-    const float* blk = k_blk + key_row(FUSED, g, bh, f) * (int64_t)nb * D;
-    for (int j = lane; j < nb; j += 64) bscore[j] = dot_f64<D>(qv, blk + (int64_t)j * D);
+  // Stage 2: the blocks of the kept frames, in batches of whole frames.
+  int c = 0, nf = 0;
+  for (;;) {
+    int nbf = 0;  // kept frames in this batch (uniform across lanes)
+    while (c < ncand && (nbf + 1) * nb <= kBlockBatch) {
+      if (fkeep[c]) {
+        const int f = ns + c;
+        if (lane == 0) bframe[nbf] = f;
+        if (sel_frames != nullptr && lane == 0 && nf < kf_stride) sel_frames[item * kf_stride + nf] = f;
+        ++nbf;
+        ++nf;
+      }
+      ++c;
+    }
+    if (nbf == 0) break;
+    __syncthreads();  // bframe is visible
+    const int nc = nbf * nb;
+    for (int r0 = 0; r0 < nc; r0 += kPerRound) {
+      const int x = r0 + sub, xc = min(x, nc - 1);
+      const int fi = xc / nb, j = xc - fi * nb;
+      const float* row = k_blk + (key_row(FUSED, g, bh, bframe[fi]) * nb + j) * (int64_t)D;
+      const double sc = dot_split<D>(qv, row, part);
+      if (x < nc && part == 0) bscore[x] = sc;
+    }
     __syncthreads();
-    rank_keep(bscore, nb, kb, bkeep, lane);
+    for (int x = lane; x < nc; x += 64) {  // rank inside the candidate's frame
+      const int fi = x / nb, j = x - fi * nb;
+      const double* seg = bscore + fi * nb;
+      const double sc = seg[j];
+      int above = 0;
+      for (int i = 0; i < nb; ++i) {
+        const double t = seg[i];
+        above += (t > sc) || (t == sc && i < j);
+      }
+      bkeep[x] = above < kb;
+    }
     __syncthreads();
-    for (int j0 = 0; j0 < nb; j0 += 64) {
-      const int j = j0 + lane;
-      const bool take = j < nb && bkeep[j];
+    for (int x0 = 0; x0 < nc; x0 += 64) {
+      const int x = x0 + lane;
+      const bool take = x < nc && bkeep[x];
       const unsigned long long m = __ballot(take);
       const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
-      if (take && at < max_sel) out[at] = f * nb + j;  // bound holds unless scores are NaN
+      if (take && at < max_sel) {  // bound holds unless scores are NaN
+        const int fi = x / nb;
+        out[at] = bframe[fi] * nb + (x - fi * nb);
+      }
       pos = min(pos + __popcll(m), max_sel);
     }
-    __syncthreads();  // bscore/bkeep are rewritten for the next kept frame
+    __syncthreads();  // bframe/bscore/bkeep are rewritten by the next batch
   }
   if (sel_frames != nullptr)
     for (int i = nf + lane; i < kf_stride; i += 64) sel_frames[item * kf_stride + i] = -1;
