@@ -110,7 +110,7 @@ constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
 // One workgroup's walk: per-wavefront query fragments and accumulators, the
 // scalar tile producer, the LDS loader and the per-tile math.
-template <typename T, int D, int WPQ, int QPWT = 4 / WPQ>
+template <typename T, int D, int WPQ, int QPWT = 4 / WPQ, bool SPLIT_PITCH = false>
 struct Walk {
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -119,19 +119,29 @@ struct Walk {
   static constexpr int NT = 64 * NW;
   static constexpr int ES = (int)sizeof(T);
   static constexpr int CPR = D * ES / 16;          // 16-byte chunks per key row
-  // LDS rows are padded by 32 bytes: consecutive rows then start 32 bytes
-  // apart modulo the 256-byte bank cycle, so eight 16-byte K reads of eight
-  // rows, and the four 32-byte row pieces a transposing V read gathers, all
-  // land on distinct banks; and every fragment address is one per-lane base
-  // plus a compile-time offset.
-  static constexpr int RS = D * ES + 32;           // LDS row stride in bytes
-  static constexpr int SPR = RS / 16;              // 16-byte slots per LDS row (CPR data + 2 pad)
-  static constexpr int TILE_SLOTS = BN * SPR;
-  static constexpr int LI = (TILE_SLOTS + NT - 1) / NT;  // load instructions per wavefront per tensor per tile
-  static constexpr int TILE_BYTES = BN * RS;
+  // LDS rows are padded so that the fragment reads of a wavefront spread
+  // over the banks, and every fragment address is one per-lane base plus a
+  // compile-time offset. K and V tiles are read differently (16-byte reads
+  // of 32 rows for K; transposing 8-byte reads that gather 4 row pieces of
+  // 32 bytes per 16 lanes for V), and no single pitch suits both: for
+  // 256-byte rows (bf16, D = 128) a 16-byte pad makes the K reads and a
+  // 64-byte pad the V reads conflict-free (measured on gfx950; the shared
+  // 32-byte pad costs both about a third of their LDS throughput). The
+  // double-buffered walk takes the split pitches; the single-stage walk
+  // keeps 32 bytes for both, since there the wider V rows' extra load
+  // instruction and pad traffic cost more than the conflicts (measured).
+  static constexpr bool kSplitPitch = SPLIT_PITCH && ES == 2 && D == 128;
+  static constexpr int RSK = D * ES + (kSplitPitch ? 16 : 32);  // K row pitch in bytes
+  static constexpr int RSV = D * ES + (kSplitPitch ? 64 : 32);  // V row pitch in bytes
+  static constexpr int SPRK = RSK / 16, SPRV = RSV / 16;       // 16-byte slots per row (CPR data + pad)
+  static constexpr int SLOTS_K = BN * SPRK, SLOTS_V = BN * SPRV;
+  static constexpr int LIK = (SLOTS_K + NT - 1) / NT;          // load instructions per wavefront per K tile
+  static constexpr int LIV = (SLOTS_V + NT - 1) / NT;          // ... per V tile
+  static constexpr int LI = LIK > LIV ? LIK : LIV;
+  static constexpr int TILE_BYTES_K = BN * RSK, TILE_BYTES_V = BN * RSV;
   static constexpr int QSTEPS = D / M::KSTEP;
   static constexpr int DB = D / 32;
-  static_assert(TILE_SLOTS % 64 == 0, "whole load instructions");
+  static_assert(SLOTS_K % 64 == 0 && SLOTS_V % 64 == 0, "whole load instructions");
 
   __device__ __forceinline__ explicit Walk(const KGeom& geom) : g(geom) {}
 
@@ -148,19 +158,9 @@ struct Walk {
   f32x16 o[DB];
   float m_run, l_run, c2;
   // producer state (uniform)
-  const uint2* walk;  // LDS table of history tiles, see the kernel
+  const uint32_t* walk;  // LDS table of history tiles, see the kernel
   int tpf, n_cur, n_tiles, all_mask, t_next, cf, ct;
   int64_t frame_elems, bh_base, cur_base;
-
-  // A tile descriptor of the walk.
-  struct Desc {
-    int64_t off;
-    int count, mask;
-    bool have;
-  };
-  // Advances d to the next tile; at the end of the walk d keeps its tile
-  // and d.have turns false.
-  __device__ __forceinline__ void advance(Desc& d) { d.have = produce(d.off, d.count, d.mask); }
 
   // Fills (off, count, mask) of the next tile: the current chunk's tiles in
   // order (counters, no divisions), then the history tiles of the table;
@@ -178,11 +178,12 @@ struct Walk {
         cur_base = bh_base + (int64_t)g.slot[g.Fh + min(cf, g.Fc - 1)] * frame_elems;
       }
     } else {
-      const uint2 e = walk[t_next - n_cur];
-      off = (int64_t)__builtin_amdgcn_readfirstlane(e.x) * D;
-      const int cm = __builtin_amdgcn_readfirstlane(e.y);
-      count = cm & 255;
-      mask = cm >> 8;
+      const uint32_t e = __builtin_amdgcn_readfirstlane(walk[t_next - n_cur]);
+      const int slot = (int)(e & 16383u), j = (int)((e >> 14) & 511u), half = (int)((e >> 23) & 1u);
+      const int start = j * g.b + half * BN;
+      off = bh_base + (int64_t)slot * frame_elems + (int64_t)start * D;
+      count = min(BN, min(j * g.b + g.b, g.T) - start);
+      mask = (int)(e >> 24);
     }
     ++t_next;
     return true;
@@ -192,16 +193,18 @@ struct Walk {
   // Load instruction i of a wavefront fills 64 consecutive 16-byte LDS slots
   // (lane l the l-th); this lane's slot holds chunk c of key row `row`, i.e.
   // byte offset row*D*ES + c*16 from the tile's first key.
-  uint32_t doff[LI];
+  uint32_t doffk[LIK], doffv[LIV];
+  static __device__ __forceinline__ uint32_t slot_offset(int slot, int spr) {
+    const int row = min(slot / spr, BN - 1);
+    int c = slot - (slot / spr) * spr;
+    while (c >= CPR) c -= CPR;  // a pad slot re-reads a chunk its row already loads (same cache line)
+    return (uint32_t)(row * D * ES + c * 16);
+  }
   __device__ __forceinline__ void init_loads() {
 #pragma unroll
-    for (int i = 0; i < LI; ++i) {
-      const int slot = (i * NW + wv) * 64 + lane;
-      const int row = min(slot / SPR, BN - 1);
-      int c = slot - (slot / SPR) * SPR;
-      c = c < CPR ? c : c - CPR;  // a pad slot re-reads a chunk its row already loads (same cache line)
-      doff[i] = (uint32_t)(row * D * ES + c * 16);
-    }
+    for (int i = 0; i < LIK; ++i) doffk[i] = slot_offset((i * NW + wv) * 64 + lane, SPRK);
+#pragma unroll
+    for (int i = 0; i < LIV; ++i) doffv[i] = slot_offset((i * NW + wv) * 64 + lane, SPRV);
   }
 
   // The next tile's loads, described at the top of an iteration and issued
@@ -233,14 +236,15 @@ struct Walk {
   // (Called with i a constant of an unrolled loop.)
   template <bool V>
   __device__ __forceinline__ void issue_one(const Next& n, int i) const {
-    if (i < LI) {
+    constexpr int NL = V ? LIV : LIK, SLOTS = V ? SLOTS_V : SLOTS_K;
+    if (i < NL) {
       const int L0 = (i * NW + wv) * 64;
       // (the buffer-to-LDS builtin exists only for the device compilation
       // pass; the host pass never runs this function)
 #if defined(__HIP_DEVICE_COMPILE__)
-      if ((i + 1) * NT <= TILE_SLOTS || L0 < TILE_SLOTS)
+      if ((i + 1) * NT <= SLOTS || L0 < SLOTS)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(V ? n.rv : n.rk, LDS_PTR(void, (V ? n.vd : n.kd) + L0 * 16), 16,
-                                                 doff[i], 0, 0, 0);
+                                                 V ? doffv[i] : doffk[i], 0, 0, 0);
 #else
       (void)n;
       (void)L0;
@@ -263,12 +267,12 @@ struct Walk {
   // ---- bf16 tile math ----------------------------------------------------
   // K fragments of key half kh (keys 32kh .. 32kh+31) for S^T = K Q^T.
   __device__ __forceinline__ void load_k(const char* ks, int kh, frag (&kf)[QSTEPS]) const {
-    const char* krow = ks + (kh * 32 + l32) * RS + h * 16;
+    const char* krow = ks + (kh * 32 + l32) * RSK + h * 16;
 #pragma unroll
     for (int t = 0; t < QSTEPS; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(krow + t * 32);
   }
   __device__ __forceinline__ frag load_k1(const char* ks, int kh, int t) const {
-    return *reinterpret_cast<const bf16x8*>(ks + (kh * 32 + l32) * RS + h * 16 + t * 32);
+    return *reinterpret_cast<const bf16x8*>(ks + (kh * 32 + l32) * RSK + h * 16 + t * 32);
   }
   // V^T fragments (A operand) of the 16-key step ps for every 32-column block.
   __device__ __forceinline__ void load_v(const char* vs, int ps, bf16x8 (&a)[DB]) const {
@@ -278,11 +282,11 @@ struct Walk {
   __device__ __forceinline__ bf16x8 load_v1(const char* vs, int ps, int db) const {
     const int s16 = lane & 15;
     // lane's key inside an 8-key group and its first column inside a 32-column block
-    const char* vbase = vs + (4 * h + (s16 >> 2)) * RS + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+    const char* vbase = vs + (4 * h + (s16 >> 2)) * RSV + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
     i16x4 part[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vbase + (16 * ps + 8 * j) * RS + 64 * db));
+      part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vbase + (16 * ps + 8 * j) * RSV + 64 * db));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
   }
   __device__ __forceinline__ void mask_half(f32x16& s, int kh, int count) const {
@@ -573,7 +577,7 @@ struct Walk {
     f32x16 s[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const char* krow = ks + (kh * 32 + l32) * RS + h * 4;
+      const char* krow = ks + (kh * 32 + l32) * RSK + h * 4;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kh][r] = 0.0f;
 #pragma unroll
@@ -608,7 +612,7 @@ struct Walk {
 #pragma unroll
     for (int ps = 0; ps < BN / 2; ++ps) {
       const int kh = ps >> 4, r = ps & 15;
-      const char* vrow = vs + (kh * 32 + acc_row(r, h)) * RS + l32 * 4;
+      const char* vrow = vs + (kh * 32 + acc_row(r, h)) * RSV + l32 * 4;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] = M::mfma(*reinterpret_cast<const frag*>(vrow + db * 128), s[kh][r], o[db]);
     }
@@ -626,19 +630,19 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ nsel, int max_sel, float scale, const KGeom g, T* __restrict__ out,
     float* __restrict__ lse) {
-  using W = Walk<T, D, WPQ, SS ? 1 : 4 / WPQ>;
+  using W = Walk<T, D, WPQ, SS ? 1 : 4 / WPQ, !SS>;
   constexpr int QPW = W::QPW, ES = W::ES, QSTEPS = W::QSTEPS, DB = W::DB;
 
   // Two named stage buffers (not one indexed array): the loop below is
   // unrolled by two so every LDS read names its buffer at compile time, which
   // lets the compiler see that reading one stage never waits on the DMA that
   // is filling the other.
-  __shared__ __attribute__((aligned(1024))) char k0[W::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v0[W::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k0[W::TILE_BYTES_K];
+  __shared__ __attribute__((aligned(1024))) char v0[W::TILE_BYTES_V];
   // History tiles of the walk, one entry each (see below); a block of more
   // than BN keys is two tiles.
   constexpr int WALK_CAP = QPW * LF_MAX_SEL * (WPQ > 2 ? 2 : 1);
-  __shared__ uint2 walk[WALK_CAP];
+  __shared__ uint32_t walk[WALK_CAP];
 
   W w(g);
   w.kc = kc;
@@ -700,13 +704,13 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
   // blocks that selected it, so a shared block is loaded once. Membership is
   // a binary search, valid when every list ascends; if one does not, no
   // block is shared (each list walks its own blocks with only its own bit),
-  // which is still exact. Entry: (cache row of the tile's first key,
-  // key count | query-block mask << 8); cache rows are counted over
-  // [B, H, S, T] and fit 32 bits (checked on the host).
+  // which is still exact. Entry (32 bits): cache slot (bits 0-13, slots are
+  // below LF_MAX_CACHE_SLOTS), block index in its frame (14-22), second
+  // BN-key tile of a longer block (23), query-block mask (24-27).
   {
     int32_t* stage = reinterpret_cast<int32_t*>(k0);
     int32_t* stage_len = stage + QPW * LF_MAX_SEL;
-    static_assert((QPW * LF_MAX_SEL + QPW) * 4 <= W::TILE_BYTES, "lists must fit in one K buffer");
+    static_assert((QPW * LF_MAX_SEL + QPW) * 4 <= W::TILE_BYTES_K, "lists must fit in one K buffer");
     const int n_hist_blocks = g.Fh * g.nb;
     const uint64_t lt = (1ull << w.lane) - 1;  // lanes below this one
     if (w.wv < QPW) {
@@ -766,10 +770,9 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
         const uint64_t b1 = __builtin_amdgcn_ballot_w64(owned), b2 = __builtin_amdgcn_ballot_w64(owned && two);
         const int pos = n_hist_tiles + __builtin_popcountll(b1 & lt) + __builtin_popcountll(b2 & lt);
         if (w.wv == 0 && owned) {
-          const int start = j * g.b, end = min(start + g.b, g.T);
-          const uint32_t row = (uint32_t)((w.bh * g.S + g.slot[f]) * g.T + start);
-          walk[pos] = make_uint2(row, (uint32_t)(min(BN, end - start) | (mask << 8)));
-          if (two) walk[pos + 1] = make_uint2(row + BN, (uint32_t)(min(BN, end - start - BN) | (mask << 8)));
+          const uint32_t e = (uint32_t)g.slot[f] | ((uint32_t)j << 14) | ((uint32_t)mask << 24);
+          walk[pos] = e;
+          if (two) walk[pos + 1] = e | (1u << 23);
         }
         n_hist_tiles += __builtin_popcountll(b1) + __builtin_popcountll(b2);
       }
@@ -822,8 +825,8 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
       c_msk = n_msk;
     }
   } else {
-  __shared__ __attribute__((aligned(1024))) char k1[W::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v1[W::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1[W::TILE_BYTES_K];
+  __shared__ __attribute__((aligned(1024))) char v1[W::TILE_BYTES_V];
   // Double-buffered walk, unrolled by two so each half names its buffers.
   // A wavefront computes a tile only if its query block selected it; with a
   // single query block per workgroup that holds for every tile (see the

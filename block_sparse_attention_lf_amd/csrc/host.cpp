@@ -36,6 +36,7 @@ lf_status make_geom(const lf_geom* g, const int32_t* frame_slot, lf::KGeom* kg) 
   if (g->hist_frames + g->chunk_frames > LF_MAX_FRAMES) return fail(LF_ERR_GEOM, "too many frames");
   if (g->n_sink < 0 || g->n_sink > g->hist_frames) return fail(LF_ERR_GEOM, "n_sink must be in [0, hist_frames]");
   if (g->cache_slots < g->hist_frames + g->chunk_frames) return fail(LF_ERR_GEOM, "cache_slots < frames named");
+  if (g->cache_slots > LF_MAX_CACHE_SLOTS) return fail(LF_ERR_GEOM, "cache_slots > LF_MAX_CACHE_SLOTS");
   const int64_t nb = (g->tokens_per_frame + (int64_t)g->block - 1) / g->block;
   if (nb > LF_MAX_BLOCKS_PER_FRAME) return fail(LF_ERR_GEOM, "too many blocks per frame");
   const int64_t lq = (int64_t)g->chunk_frames * g->tokens_per_frame;

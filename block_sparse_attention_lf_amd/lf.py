@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(HERE, "liblf.so")
 LF_F32, LF_BF16 = 0, 1
 LF_CACHE_ROLLING, LF_CACHE_ANCHORED = 0, 1
 LF_MAX_FRAMES, LF_MAX_BLOCKS_PER_FRAME, LF_MAX_BLOCK, LF_MAX_SEL, LF_MAX_CANDIDATES_1D = 256, 512, 128, 512, 4096
+LF_MAX_CACHE_SLOTS = 16384
 
 STATUS = {0: "LF_OK", -1: "LF_ERR_NULL", -2: "LF_ERR_GEOM", -3: "LF_ERR_DTYPE", -4: "LF_ERR_K",
           -5: "LF_ERR_ALIGN", -6: "LF_ERR_HIP", -7: "LF_ERR_SLOT", -8: "LF_ERR_ARG"}

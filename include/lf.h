@@ -75,6 +75,9 @@ typedef enum { LF_CACHE_ROLLING = 0, LF_CACHE_ANCHORED = 1 } lf_cache_policy;
 #define LF_MAX_FRAMES 256
 /* Most blocks per frame (nb) the selection supports. */
 #define LF_MAX_BLOCKS_PER_FRAME 512
+/* Most cache slots (S) of a cache (a slot index is a 14-bit field of the
+ * attention kernel's tile table). */
+#define LF_MAX_CACHE_SLOTS 16384
 /* Largest block (tokens) the attention kernel supports. */
 #define LF_MAX_BLOCK 128
 /* Most selected blocks per query block the attention kernel reads (max_sel). */
@@ -91,7 +94,7 @@ typedef struct {
   int32_t chunk_frames;     /* Fc >= 1 */
   int32_t hist_frames;      /* Fh >= 0; Fh + Fc <= LF_MAX_FRAMES */
   int32_t n_sink;           /* 0 <= n_sink <= Fh */
-  int32_t cache_slots;      /* >= Fh + Fc; B*H*cache_slots*T < 2^32 */
+  int32_t cache_slots;      /* >= Fh + Fc, <= LF_MAX_CACHE_SLOTS; B*H*cache_slots*T < 2^32 */
   int32_t dtype;            /* lf_dtype */
 } lf_geom;
 

@@ -95,7 +95,8 @@ def _raw_compress(g, slots):
 
 @pytest.mark.parametrize("field,value,status", [("head_dim", 96, -2), ("dtype", 7, -3), ("block", 0, -2),
                                                 ("block", 129, -2), ("n_sink", 7, -2), ("cache_slots", 8, -2),
-                                                ("tokens_per_frame", 0, -2), ("heads", 0, -2)])
+                                                ("tokens_per_frame", 0, -2), ("heads", 0, -2),
+                                                ("cache_slots", 16385, -2)])
 def test_invalid_geometry_is_rejected_before_launch(field, value, status):
     w = I.WAN480P_CHUNK
     g = lf.geom_of(w)
