@@ -34,7 +34,9 @@ Readings where the pages leave a step open (each restated at its function):
   R8 sink frames are always attended in full and are not top-k candidates;
   R15 ties in a top-k go to the lowest index;
   R18 the single-level ("1D") ablation variant ranks all non-sink history
-      blocks in one top-k.
+      blocks in one top-k;
+  R19 the backward pass is the gradient of the loss sum(out * dout) through
+      the same masks (the selection itself is not differentiated).
 Pooling sums in float64 and rounds the mean once to float32; scores are
 float64 dot products of those float32 values; attention is float64 dense
 masked softmax.
@@ -304,6 +306,75 @@ def attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, frame_slo
         out[b, h, rows] = o
         lse[b, h, rows] = l
     return {"out": out, "lse": lse}
+
+
+def masked_softmax_attention_grad(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray, scale: float,
+                                  dout: np.ndarray):
+    """Gradients of ``masked_softmax_attention`` for the loss sum(O * dout), float64.
+
+    Chain rule through O = P v, P = softmax(S) row-wise, S = scale q k^T with
+    masked entries fixed at -inf:
+      dV = P^T dO;   dP = dO v^T;   D_i = sum_j P_ij dP_ij (= dO_i . O_i);
+      dS = P * (dP - D);   dq = scale dS k;   dk = scale dS^T q.
+    Masked entries have P = 0, so they pass no gradient. Returns dq [n, d],
+    dk [L, d], dv [L, d].
+    Pinned by tests/test_oracle_backward.py (central finite differences of
+    the forward oracle, autograd of an independent torch formulation, and
+    the sum rules sum_j dk_j = 0, sum_j dv_j = sum_i dO_i).
+    """
+    o, _, p = masked_softmax_attention(q, k, v, mask, scale)
+    dout = np.asarray(dout, np.float64)
+    dv = p.T @ dout
+    dp = dout @ np.asarray(v, np.float64).T
+    dd = np.sum(dout * o, axis=1, keepdims=True)
+    ds = p * (dp - dd)
+    dq = scale * (ds @ np.asarray(k, np.float64))
+    dk = scale * (ds.T @ np.asarray(q, np.float64))
+    return dq, dk, dv
+
+
+def attention_grad(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, frame_slot: Sequence[int],
+                   sel_blocks: np.ndarray, n_sel: np.ndarray, dout: np.ndarray, tokens_per_frame: int, block: int,
+                   chunk_frames: int, hist_frames: int, scale: float) -> Dict[str, np.ndarray]:
+    """Backward of ``attention`` for the loss sum(out * dout) (the gradient a
+    sparse fine-tuning step needs; the ablation passage of the technical
+    summary fine-tunes with the sparse attention in place).
+
+    Each query block contributes through its own mask; key and value
+    gradients of one cache row add up over every query block that sees it.
+    Rows of cache slots that ``frame_slot`` does not name get zero.
+    Returns dq [B,H,Lq,d], dk_cache and dv_cache [B,H,S,T,d], float64.
+    """
+    B, H, Lq, d = q.shape
+    S = k_cache.shape[2]
+    T = tokens_per_frame
+    ranges = block_ranges(T, block)
+    nb = len(ranges)
+    nqb = chunk_frames * nb
+    n_frames = hist_frames + chunk_frames
+    dq = np.zeros((B, H, Lq, d))
+    dk_cache = np.zeros((B, H, S, T, d))
+    dv_cache = np.zeros((B, H, S, T, d))
+    for b in range(B):
+        for h in range(H):
+            K = logical_sequence(k_cache[b, h], frame_slot, n_frames)
+            V = logical_sequence(v_cache[b, h], frame_slot, n_frames)
+            dK = np.zeros_like(K)
+            dV = np.zeros_like(V)
+            for qb in range(nqb):
+                fc, j = divmod(qb, nb)
+                s, e = ranges[j]
+                rows = slice(fc * T + s, fc * T + e)
+                ids = sel_blocks[b, h, qb, :n_sel[b, h, qb]]
+                mask = visible_keys(ids, T, block, hist_frames, chunk_frames)
+                gq, gk, gv = masked_softmax_attention_grad(q[b, h, rows], K, V, mask, scale, dout[b, h, rows])
+                dq[b, h, rows] = gq
+                dK += gk
+                dV += gv
+            for f in range(n_frames):
+                dk_cache[b, h, frame_slot[f]] = dK[f * T:(f + 1) * T]
+                dv_cache[b, h, frame_slot[f]] = dV[f * T:(f + 1) * T]
+    return {"dq": dq, "dk_cache": dk_cache, "dv_cache": dv_cache}
 
 
 # ---------------------------------------------------------------------------
