@@ -32,20 +32,11 @@
 //     i&3 of source lane 4e+(i>>2), i.e. four consecutive keys of one column.
 //   * exp2 with the scale folded into log2(e) units; rows past the end of a
 //     ragged query block are computed on zero queries and never stored.
-#include "lf_internal.h"
+#include "mfma.h"
 
 namespace lf {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int BN = 64;     // keys per tile
 // bf16 blocks of 33..64 keys use the single-stage kernel (one query block
 // per workgroup) instead of the double-buffered one.
@@ -81,10 +72,6 @@ __device__ inline P* uniform_ptr(P* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
 }
-
-// Key index held by accumulator register r of lane half h in a 32x32 MFMA
-// output (rows = keys): 8*(r/4) + 4*h + r%4.
-__device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
 // Pins a computed value at this point of the program: an empty asm that
 // claims to modify the register, so no optimisation pass moves the

@@ -1,0 +1,402 @@
+// Backward of the block-sparse attention (gradients of sum(out * dout)
+// through the same block masks), for sparse fine-tuning: the ablation
+// passage of the Light Forcing technical summary fine-tunes the model with
+// the sparse attention in place. With S = scale q k^T over the keys a query
+// block sees, P = softmax(S), O = P v:
+//   dV = P^T dO,  dP = dO v^T,  D_i = dO_i . O_i,  dS = P * (dP - D),
+//   dq = scale dS k,  dk = scale dS^T q.
+// P is recomputed from the forward's log-sum-exp: P = exp2(scale*log2(e)*s
+// - lse*log2(e)).
+//
+// gfx950 design (bf16 inputs, float32 gradients, MFMA 32x32x16 bf16 with
+// float32 accumulation; P and dS are rounded to bf16 as MFMA operands):
+//   * bwd_dq_kernel: one workgroup per query block (one wavefront per 32
+//     rows), walking the same tiles as the forward (the current chunk's
+//     64-key tiles, then the blocks of its selection). Per 32-key half:
+//     S^T = K Q^T and dP^T = V dO^T (Q^T, dO^T in registers), dS^T, then
+//     dQ^T += K^T dS^T with K^T read from the row-major tile by the
+//     transposing LDS read. It also writes D_i = dO_i . O_i for the key pass.
+//   * bwd_dkv_kernel: one workgroup per key tile (one wavefront per 32
+//     keys), walking the query blocks that see the tile (all of them for a
+//     current-chunk tile; those whose selection holds the block for a history
+//     tile). Per 32 query rows: S = Q K^T (K^T in registers), P; the dV pass
+//     adds dO^T P, the dK pass dP = dO V^T, dS and Q^T dS. Splitting dK and
+//     dV into two passes keeps each under 256 registers (two wavefronts per
+//     SIMD) at the price of computing S twice.
+//   Each key row's gradient is summed inside one workgroup: no atomics, and
+//   every gradient row of a frame named by the slot table is written once
+//   (zero where no query sees it). Rows of other slots are not written.
+#include "mfma.h"
+
+namespace lf {
+namespace {
+
+template <int D>
+struct BwdShape {
+  static constexpr int RS = D * 2 + 32;  // LDS row pitch (bytes): bf16 row + 32-byte pad
+  static constexpr int CPR = D * 2 / 16;  // 16-byte chunks per row
+  static constexpr int QSTEPS = D / 16;   // MFMA reduction steps over d
+  static constexpr int DB = D / 32;       // 32-column blocks of d
+};
+
+// Rows [0, count) of a row-major [*, D] bf16 matrix into LDS at pitch RS;
+// rows [count, rows) become zeros. All threads of the workgroup take part.
+template <int D>
+__device__ inline void stage_rows(char* lds, const __bf16* src, int count, int rows, int tid, int nthreads) {
+  using S = BwdShape<D>;
+  for (int i = tid; i < rows * S::CPR; i += nthreads) {
+    const int r = i / S::CPR, c = i - r * S::CPR;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < count) v = *reinterpret_cast<const uint4*>(src + (int64_t)r * D + c * 8);
+    *reinterpret_cast<uint4*>(lds + r * S::RS + c * 16) = v;
+  }
+}
+
+// MFMA operand fragments (lane l, l32 = l % 32, h = l / 32):
+// rows r0 + l32 of an LDS tile, d = 16t + 8h .. +7 (A operand, rows = M).
+template <int D>
+__device__ inline bf16x8 row_frag(const char* tile, int r0, int t, int l32, int h) {
+  return *reinterpret_cast<const bf16x8*>(tile + (r0 + l32) * BwdShape<D>::RS + (16 * t + 8 * h) * 2);
+}
+// The transposed fragment of 16 rows (step ps) and 32 columns (block db):
+// A[d][row] with the rows in the order a 32x32 accumulator holds them, so
+// the bf16 copy of an accumulator is the matching B operand.
+template <int D>
+__device__ inline bf16x8 tr_frag(const char* tile, int ps, int db, int lane) {
+  constexpr int RS = BwdShape<D>::RS;
+  const int s16 = lane & 15, h = lane >> 5;
+  const char* base = tile + (4 * h + (s16 >> 2)) * RS + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+  i16x4 part[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + (16 * ps + 8 * j) * RS + 64 * db));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// This lane's own row of a global matrix, d = 16t + 8h .. +7 (B operand,
+// column = the lane's row), zeros when the row does not exist.
+__device__ inline bf16x8 own_frag(const __bf16* row, bool ok, int t, int h) {
+  const uint4 v = ok ? *reinterpret_cast<const uint4*>(row + 16 * t + 8 * h) : make_uint4(0u, 0u, 0u, 0u);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Writes a transposed 32x32 accumulator block (rows = d in [32db, 32db+32),
+// column = this lane's row) times `mul` as float32 into row `dst`.
+__device__ inline void store_acc_t(float* dst, const f32x16& acc, int db, int h, float mul) {
+#pragma unroll
+  for (int a4 = 0; a4 < 4; ++a4) {
+    const int col = db * 32 + 8 * a4 + 4 * h;
+    *reinterpret_cast<float4*>(dst + col) = make_float4(acc[4 * a4] * mul, acc[4 * a4 + 1] * mul,
+                                                       acc[4 * a4 + 2] * mul, acc[4 * a4 + 3] * mul);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and D_i): one workgroup of WPQ wavefronts per (batch, head, query block).
+template <int D, int WPQ>
+__global__ __launch_bounds__(64 * WPQ) void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
+                                                          const __bf16* __restrict__ vc, const __bf16* __restrict__ out,
+                                                          const __bf16* __restrict__ dout, const float* __restrict__ lse,
+                                                          const int32_t* __restrict__ sel,
+                                                          const int32_t* __restrict__ nsel, int max_sel, float scale,
+                                                          const KGeom g, float* __restrict__ delta,
+                                                          float* __restrict__ dq) {
+  using S = BwdShape<D>;
+  constexpr int NT = 64 * WPQ;
+  __shared__ __attribute__((aligned(16))) char ks[64 * S::RS];
+  __shared__ __attribute__((aligned(16))) char vs[64 * S::RS];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t item = blockIdx.x;  // (b*H + h)*nqb + qb
+  const int64_t bh = item / g.nqb;
+  const int qb = (int)(item - bh * g.nqb);
+  const int fc = qb / g.nb, jq = qb - fc * g.nb;
+  const int nrows = min(g.b, g.T - jq * g.b);
+  const int64_t row0 = bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b;
+  const int qr = 32 * wv + l32;
+  const bool ok = qr < nrows;
+  const float c2 = scale * kLog2e;
+
+  bf16x8 qf[S::QSTEPS], dof[S::QSTEPS];
+  float dd = 0.0f;
+  {
+    const __bf16* qp = q + (row0 + (ok ? qr : 0)) * D;
+    const __bf16* gp = dout + (row0 + (ok ? qr : 0)) * D;
+    const __bf16* op = out + (row0 + (ok ? qr : 0)) * D;
+#pragma unroll
+    for (int t = 0; t < S::QSTEPS; ++t) {
+      qf[t] = own_frag(qp, ok, t, h);
+      dof[t] = own_frag(gp, ok, t, h);
+      const bf16x8 of = own_frag(op, ok, t, h);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dd = fmaf((float)dof[t][e], (float)of[e], dd);
+    }
+  }
+  dd += __shfl_xor(dd, 32);  // the other half of the row's d
+  if (ok && h == 0) delta[row0 + qr] = dd;
+  const float lse2 = ok ? lse[row0 + qr] * kLog2e : 0.0f;
+
+  f32x16 acc[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+
+  const int tpf = (g.T + 63) / 64;
+  const int n_cur = g.Fc * tpf;
+  const int hpb = g.b > 64 ? 2 : 1;
+  const int len = max_sel > 0 ? min(max(nsel[item], 0), max_sel) : 0;
+  const int n_hist_blocks = g.Fh * g.nb;
+  for (int t = 0; t < n_cur + len * hpb; ++t) {
+    int slot, start, count;
+    if (t < n_cur) {
+      const int f2 = t / tpf, tt = t - f2 * tpf;
+      slot = g.slot[g.Fh + f2];
+      start = tt * 64;
+      count = min(64, g.T - start);
+    } else {
+      const int e = (t - n_cur) / hpb, half = (t - n_cur) - e * hpb;
+      const int x = sel[item * max_sel + e];
+      if (x < 0 || x >= n_hist_blocks) continue;  // ignored id (uniform: every wavefront skips it)
+      const int f = x / g.nb, jb = x - f * g.nb;
+      slot = g.slot[f];
+      start = jb * g.b + half * 64;
+      count = min(64, min(jb * g.b + g.b, g.T) - start);
+      if (count <= 0) continue;
+    }
+    const int64_t base = ((bh * g.S + slot) * (int64_t)g.T + start) * D;
+    __syncthreads();  // the previous tile's reads are done
+    stage_rows<D>(ks, kc + base, count, 64, tid, NT);
+    stage_rows<D>(vs, vc + base, count, 64, tid, NT);
+    __syncthreads();
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.0f;
+        dp[r] = 0.0f;
+      }
+#pragma unroll
+      for (int st = 0; st < S::QSTEPS; ++st) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(ks, 32 * kh, st, l32, h), qf[st], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vs, 32 * kh, st, l32, h), dof[st], dp, 0, 0, 0);
+      }
+      bf16x8 b0, b1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool kv = 32 * kh + acc_row(r, h) < count;
+        const float p = kv ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2)) : 0.0f;
+        const __bf16 d = (__bf16)(p * (dp[r] - dd));
+        if (r < 8) b0[r] = d; else b1[r - 8] = d;
+      }
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) {
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ks, 2 * kh, db, lane), b0, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ks, 2 * kh + 1, db, lane), b1, acc[db], 0, 0, 0);
+      }
+    }
+  }
+  if (!ok) return;
+  float* dst = dq + (row0 + qr) * D;
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db) store_acc_t(dst, acc[db], db, h, scale);
+}
+
+// ---------------------------------------------------------------------------
+// dK (DK) or dV: one workgroup of two wavefronts per key tile of one (batch,
+// head). Tiles per (batch, head): the current chunk's Fc * ceil(T/64) tiles,
+// then every history block's tile(s) (blocks of more than 64 keys are two).
+template <int D, int MAXQ, bool DK>
+__global__ __launch_bounds__(128) void bwd_dkv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
+                                                      const __bf16* __restrict__ vc, const __bf16* __restrict__ dout,
+                                                      const float* __restrict__ lse, const float* __restrict__ delta,
+                                                      const int32_t* __restrict__ sel,
+                                                      const int32_t* __restrict__ nsel, int max_sel, float scale,
+                                                      const KGeom g, float* __restrict__ dst) {
+  using S = BwdShape<D>;
+  constexpr int NT = 128;
+  __shared__ __attribute__((aligned(16))) char qs[MAXQ * S::RS];
+  __shared__ __attribute__((aligned(16))) char gs[MAXQ * S::RS];
+  __shared__ float lse2s[MAXQ];
+  __shared__ float dds[MAXQ];
+  __shared__ int qlist[64];
+  __shared__ int qcount;
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tpf = (g.T + 63) / 64;
+  const int n_cur = g.Fc * tpf;
+  const int hpb = g.b > 64 ? 2 : 1;
+  const int per_bh = n_cur + g.Fh * g.nb * hpb;
+  const int64_t bh = blockIdx.x / per_bh;
+  const int ti = (int)(blockIdx.x - bh * per_bh);
+  int f, start, count, hist_id = -1;
+  if (ti < n_cur) {
+    const int f2 = ti / tpf;
+    f = g.Fh + f2;
+    start = (ti - f2 * tpf) * 64;
+    count = min(64, g.T - start);
+  } else {
+    const int hi = ti - n_cur;
+    f = hi / (g.nb * hpb);
+    const int rem = hi - f * g.nb * hpb;
+    const int jb = rem / hpb, half = rem - jb * hpb;
+    start = jb * g.b + half * 64;
+    count = min(64, min(jb * g.b + g.b, g.T) - start);
+    hist_id = f * g.nb + jb;
+  }
+  if (count <= 0) return;  // second half of a short last block: no keys (uniform over the workgroup)
+  const int64_t krow0 = (bh * g.S + g.slot[f]) * (int64_t)g.T + start;
+  const int key = 32 * wv + l32;
+  const bool kok = key < count;
+  const float c2 = scale * kLog2e;
+
+  bf16x8 kf[S::QSTEPS], vf[S::QSTEPS];
+#pragma unroll
+  for (int t = 0; t < S::QSTEPS; ++t) {
+    kf[t] = own_frag(kc + (krow0 + (kok ? key : 0)) * D, kok, t, h);
+    if constexpr (DK) vf[t] = own_frag(vc + (krow0 + (kok ? key : 0)) * D, kok, t, h);
+  }
+  f32x16 acc[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+
+  // Query blocks that see this tile, 64 candidates at a time.
+  for (int c0 = 0; c0 < g.nqb; c0 += 64) {
+    __syncthreads();  // every wavefront has read the previous batch's list and count
+    if (wv == 0) {
+      const int qb = c0 + lane;
+      bool sees = qb < g.nqb;
+      if (sees && hist_id >= 0) {
+        const int64_t item = bh * g.nqb + qb;
+        const int len = max_sel > 0 ? min(max(nsel[item], 0), max_sel) : 0;
+        bool found = false;
+        for (int e = 0; e < len; ++e) found = found || sel[item * max_sel + e] == hist_id;
+        sees = found;
+      }
+      const uint64_t m = __builtin_amdgcn_ballot_w64(sees);
+      if (sees) qlist[__builtin_popcountll(m & ((1ull << lane) - 1ull))] = qb;
+      if (lane == 0) qcount = __builtin_popcountll(m);
+    }
+    __syncthreads();
+    const int nq = qcount;
+    for (int i = 0; i < nq; ++i) {
+      const int qb = qlist[i];
+      const int fc = qb / g.nb, jq = qb - fc * g.nb;
+      const int nrows = min(g.b, g.T - jq * g.b);
+      const int64_t row0 = bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b;
+      const int halves = (nrows + 31) / 32;
+      stage_rows<D>(qs, q + row0 * D, nrows, 32 * halves, tid, NT);
+      stage_rows<D>(gs, dout + row0 * D, nrows, 32 * halves, tid, NT);
+      for (int r = tid; r < 32 * halves; r += NT) {
+        lse2s[r] = r < nrows ? lse[row0 + r] * kLog2e : INFINITY;  // +inf: P = 0 on missing rows
+        if constexpr (DK) dds[r] = r < nrows ? delta[row0 + r] : 0.0f;
+      }
+      __syncthreads();
+      for (int qh = 0; qh < halves; ++qh) {
+        f32x16 s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+        for (int st = 0; st < S::QSTEPS; ++st)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qs, 32 * qh, st, l32, h), kf[st], s, 0, 0, 0);
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          p[r] = kok ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2s[32 * qh + acc_row(r, h)])) : 0.0f;
+        bf16x8 b0, b1;
+        if constexpr (DK) {
+          f32x16 dp;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dp[r] = 0.0f;
+#pragma unroll
+          for (int st = 0; st < S::QSTEPS; ++st)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(gs, 32 * qh, st, l32, h), vf[st], dp, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const __bf16 d = (__bf16)(p[r] * (dp[r] - dds[32 * qh + acc_row(r, h)]));
+            if (r < 8) b0[r] = d; else b1[r - 8] = d;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if (r < 8) b0[r] = (__bf16)p[r]; else b1[r - 8] = (__bf16)p[r];
+          }
+        }
+        const char* at = DK ? qs : gs;  // dK^T += Q^T dS; dV^T += dO^T P
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db) {
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(at, 2 * qh, db, lane), b0, acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(at, 2 * qh + 1, db, lane), b1, acc[db], 0, 0, 0);
+        }
+      }
+      __syncthreads();  // the staged rows are rewritten by the next query block
+    }
+  }
+  if (!kok) return;
+  float* row = dst + (krow0 + key) * D;
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db) store_acc_t(row, acc[db], db, h, DK ? scale : 1.0f);
+}
+
+template <int D>
+hipError_t launch_bwd_d(const KGeom& g, const void* q, const void* k, const void* v, const int32_t* sel,
+                        const int32_t* nsel, int max_sel, float scale, const void* out, const float* lse,
+                        const void* dout, float* delta, float* dq, float* dk, float* dv, hipStream_t stream) {
+  const __bf16* Q = static_cast<const __bf16*>(q);
+  const __bf16* K = static_cast<const __bf16*>(k);
+  const __bf16* V = static_cast<const __bf16*>(v);
+  const __bf16* O = static_cast<const __bf16*>(out);
+  const __bf16* G = static_cast<const __bf16*>(dout);
+  const unsigned nq = (unsigned)((int64_t)g.B * g.H * g.nqb);
+  switch ((g.b + 31) / 32) {
+    case 1:
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 1>), dim3(nq), dim3(64), 0, stream, Q, K, V, O, G, lse, sel, nsel, max_sel,
+                         scale, g, delta, dq);
+      break;
+    case 2:
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), dim3(nq), dim3(128), 0, stream, Q, K, V, O, G, lse, sel, nsel,
+                         max_sel, scale, g, delta, dq);
+      break;
+    case 3:
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 3>), dim3(nq), dim3(192), 0, stream, Q, K, V, O, G, lse, sel, nsel,
+                         max_sel, scale, g, delta, dq);
+      break;
+    default:
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), dim3(nq), dim3(256), 0, stream, Q, K, V, O, G, lse, sel, nsel,
+                         max_sel, scale, g, delta, dq);
+      break;
+  }
+  const int tpf = (g.T + 63) / 64;
+  const unsigned nk = (unsigned)((int64_t)g.B * g.H * (g.Fc * tpf + g.Fh * g.nb * (g.b > 64 ? 2 : 1)));
+  if (g.b <= 64) {
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 64, false>), dim3(nk), dim3(128), 0, stream, Q, K, V, G, lse, delta, sel,
+                       nsel, max_sel, scale, g, dv);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 64, true>), dim3(nk), dim3(128), 0, stream, Q, K, V, G, lse, delta, sel,
+                       nsel, max_sel, scale, g, dk);
+  } else {
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 128, false>), dim3(nk), dim3(128), 0, stream, Q, K, V, G, lse, delta, sel,
+                       nsel, max_sel, scale, g, dv);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 128, true>), dim3(nk), dim3(128), 0, stream, Q, K, V, G, lse, delta, sel,
+                       nsel, max_sel, scale, g, dk);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_bwd(const KGeom& g, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel, float scale,
+                                const void* out, const float* lse, const void* dout, float* delta, float* dq,
+                                float* dk_cache, float* dv_cache, hipStream_t stream) {
+  if (g.D == 128)
+    return launch_bwd_d<128>(g, q, k_cache, v_cache, sel_blocks, n_sel, max_sel, scale, out, lse, dout, delta, dq,
+                             dk_cache, dv_cache, stream);
+  return launch_bwd_d<64>(g, q, k_cache, v_cache, sel_blocks, n_sel, max_sel, scale, out, lse, dout, delta, dq,
+                          dk_cache, dv_cache, stream);
+}
+
+}  // namespace lf

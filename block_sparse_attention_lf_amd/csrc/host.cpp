@@ -230,6 +230,32 @@ lf_status lf_block_sparse_attn(const lf_geom* g, const void* q, const void* k_ca
                     "lf_block_sparse_attn launch");
 }
 
+lf_status lf_block_sparse_attn_bwd(const lf_geom* g, const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* frame_slot, const int32_t* sel_blocks, const int32_t* n_sel,
+                                   int32_t max_sel, float softmax_scale, const void* out, const float* lse,
+                                   const void* dout, float* delta, float* dq, float* dk_cache, float* dv_cache,
+                                   lf_stream stream) {
+  if (frame_slot == nullptr) return fail(LF_ERR_NULL, "frame_slot is NULL");
+  lf::KGeom kg;
+  lf_status st = make_geom(g, frame_slot, &kg);
+  if (st != LF_OK) return st;
+  if (g->dtype != LF_BF16) return fail(LF_ERR_DTYPE, "the backward takes bf16 inputs");
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr || lse == nullptr ||
+      dout == nullptr || delta == nullptr || dq == nullptr || dk_cache == nullptr || dv_cache == nullptr)
+    return fail(LF_ERR_NULL, "an input or output of the backward is NULL");
+  if (max_sel < 0 || max_sel > LF_MAX_SEL) return fail(LF_ERR_K, "max_sel must be in [0, LF_MAX_SEL]");
+  if (max_sel > 0 && (sel_blocks == nullptr || n_sel == nullptr))
+    return fail(LF_ERR_NULL, "sel_blocks / n_sel is NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk_cache) || !aligned16(dv_cache))
+    return fail(LF_ERR_ALIGN, "q / caches / out / dout / gradients must be 16-byte aligned");
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return fail(LF_ERR_ARG, "softmax_scale must be > 0");
+  return hip_status(lf::launch_attention_bwd(kg, q, k_cache, v_cache, sel_blocks, n_sel, max_sel, softmax_scale, out,
+                                             lse, dout, delta, dq, dk_cache, dv_cache,
+                                             static_cast<hipStream_t>(stream)),
+                    "lf_block_sparse_attn_bwd launch");
+}
+
 lf_status lf_chunk_budget(int32_t n_chunks, const double* sigma, const double* weight, const uint8_t* dense,
                           double s_base, double s_target, const int32_t* hist_frames, const int32_t* n_sink,
                           int32_t blocks_per_frame, int32_t k_frames_min, double* sparsity_out, double* beta_out,

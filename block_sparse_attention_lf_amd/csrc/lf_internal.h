@@ -38,5 +38,11 @@ hipError_t launch_select_blocks(const KGeom& g, const float* q_blk, const float*
 hipError_t launch_attention(const KGeom& g, int32_t dtype, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel, float scale,
                             void* out, float* lse, hipStream_t stream);
+// Backward of launch_attention (bf16): dq [B,H,Lq,D], dk/dv rows of the
+// frames in g.slot, delta [B,H,Lq] scratch; all float32.
+hipError_t launch_attention_bwd(const KGeom& g, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel, float scale,
+                                const void* out, const float* lse, const void* dout, float* delta, float* dq,
+                                float* dk_cache, float* dv_cache, hipStream_t stream);
 
 }  // namespace lf

@@ -30,7 +30,7 @@ STATUS = {0: "LF_OK", -1: "LF_ERR_NULL", -2: "LF_ERR_GEOM", -3: "LF_ERR_DTYPE", 
 
 # Every symbol include/lf.h declares.
 EXPORTS = ("lf_compress", "lf_max_sel", "lf_select", "lf_max_sel_1d", "lf_select_blocks", "lf_pool_keys", "lf_select_fused", "lf_block_sparse_attn",
-           "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error")
+           "lf_block_sparse_attn_bwd", "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error")
 
 
 class LfError(RuntimeError):
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         "lf_select_blocks": (ctypes.c_int, [G, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P]),
         "lf_block_sparse_attn": (ctypes.c_int, [G, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32, ctypes.c_float,
                                                 _P, _P, _P]),
+        "lf_block_sparse_attn_bwd": (ctypes.c_int, [G, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32, ctypes.c_float,
+                                                    _P, _P, _P, _P, _P, _P, _P, _P]),
         "lf_chunk_budget": (ctypes.c_int, [ctypes.c_int32, _F64P, _F64P, ctypes.POINTER(ctypes.c_uint8),
                                            ctypes.c_double, ctypes.c_double, _I32P, _I32P, ctypes.c_int32,
                                            ctypes.c_int32, _F64P, _F64P, _I32P, _I32P]),
@@ -245,6 +247,31 @@ def lf_block_sparse_attn(g: lf_geom, q, k_cache, v_cache, frame_slot, sel_blocks
     _check(lib().lf_block_sparse_attn(ctypes.byref(g), _ptr(q), _ptr(k_cache), _ptr(v_cache), sp, _ptr(sel_blocks),
                                       _ptr(n_sel), max_sel, float(softmax_scale), _ptr(out), _ptr(lse),
                                       _stream(stream)), "lf_block_sparse_attn")
+
+
+def lf_block_sparse_attn_bwd(g: lf_geom, q, k_cache, v_cache, frame_slot, sel_blocks, n_sel, softmax_scale: float,
+                             out, lse, dout, delta, dq, dk_cache, dv_cache, stream=None) -> None:
+    """Backward of lf_block_sparse_attn (see include/lf.h): float32 dq, dk_cache, dv_cache."""
+    D = g.head_dim
+    _need(q, (g.batch, g.heads, g.q_len, D), torch.bfloat16, "q")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, (g.batch, g.heads, g.cache_slots, g.tokens_per_frame, D), torch.bfloat16, name)
+    for name, t in (("out", out), ("dout", dout)):
+        _need(t, (g.batch, g.heads, g.q_len, D), torch.bfloat16, name)
+    for name, t in (("lse", lse), ("delta", delta)):
+        _need(t, (g.batch, g.heads, g.q_len), torch.float32, name)
+    _need(dq, (g.batch, g.heads, g.q_len, D), torch.float32, "dq")
+    for name, t in (("dk_cache", dk_cache), ("dv_cache", dv_cache)):
+        _need(t, (g.batch, g.heads, g.cache_slots, g.tokens_per_frame, D), torch.float32, name)
+    max_sel = 0 if sel_blocks is None else sel_blocks.shape[-1]
+    if sel_blocks is not None:
+        _need(sel_blocks, (g.batch, g.heads, g.n_qblocks, max_sel), torch.int32, "sel_blocks")
+        _need(n_sel, (g.batch, g.heads, g.n_qblocks), torch.int32, "n_sel")
+    arr, sp = _slots(frame_slot)
+    _check(lib().lf_block_sparse_attn_bwd(ctypes.byref(g), _ptr(q), _ptr(k_cache), _ptr(v_cache), sp,
+                                          _ptr(sel_blocks), _ptr(n_sel), max_sel, float(softmax_scale), _ptr(out),
+                                          _ptr(lse), _ptr(dout), _ptr(delta), _ptr(dq), _ptr(dk_cache),
+                                          _ptr(dv_cache), _stream(stream)), "lf_block_sparse_attn_bwd")
 
 
 def lf_chunk_budget(sigma, weight, dense, s_base: float, s_target: float, hist_frames, n_sink, blocks_per_frame: int,

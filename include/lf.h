@@ -9,7 +9,8 @@
  *              2.1 chunk-aware growth (CAG), 2.2 hierarchical sparse attention
  *              (HSA: token compression, two-stage mask selection, execution).
  *   [LF-press] press summary of the same paper, section 3 (hierarchical
- *              sparse attention) and section 2 (chunk-aware growth).
+ *              sparse attention), section 2 (chunk-aware growth) and
+ *              section 4 (experiments, ablation paragraph).
  *   [SF]       Self Forcing news page, rolling KV cache paragraph.
  *   [RF]       Rolling Forcing page, section 3, dual cache / attention anchor.
  *
@@ -187,6 +188,28 @@ lf_status lf_select_blocks(const lf_geom* g, const float* q_blk, const float* k_
 lf_status lf_block_sparse_attn(const lf_geom* g, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* frame_slot, const int32_t* sel_blocks, const int32_t* n_sel,
                                int32_t max_sel, float softmax_scale, void* out, float* lse, lf_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward of lf_block_sparse_attn, for sparse fine-tuning ([LF-press] 4,
+ * ablation paragraph: the sparse attention is fine-tuned in place; the
+ * gradients below are those of the loss sum(out * dout) through the same
+ * block masks, the selection itself not being differentiated).
+ * Inputs: the forward's q, caches, frame_slot, sel_blocks / n_sel / max_sel
+ * and softmax_scale, its outputs out [B,H,Lq,D] and lse [B,H,Lq] (float32,
+ * as lf_block_sparse_attn writes them), and dout [B,H,Lq,D]. q, caches, out
+ * and dout are bf16 (g->dtype must be LF_BF16, else LF_ERR_DTYPE).
+ * Outputs, float32: dq [B,H,Lq,D]; dk_cache and dv_cache [B,H,S,T,D], where
+ * every row of a slot that frame_slot names gets its full gradient (summed
+ * over all query blocks that see it; zero if none does) and rows of other
+ * slots are left untouched; delta [B,H,Lq] is scratch the call writes
+ * (rowsum(dout * out)). P and dS enter the MFMAs rounded to bf16, with
+ * float32 accumulation. Same validation and error codes as the forward.
+ * ------------------------------------------------------------------------- */
+lf_status lf_block_sparse_attn_bwd(const lf_geom* g, const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* frame_slot, const int32_t* sel_blocks, const int32_t* n_sel,
+                                   int32_t max_sel, float softmax_scale, const void* out, const float* lse,
+                                   const void* dout, float* delta, float* dq, float* dk_cache, float* dv_cache,
+                                   lf_stream stream);
 
 /* ---------------------------------------------------------------------------
  * Chunk-aware growth budget ([LF-tech] 2.1; [LF-press] 2). Host only.

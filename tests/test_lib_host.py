@@ -181,3 +181,22 @@ def test_pool_keys_validation():
     assert call([0], n=-1) == -8
     assert call([0], n=lf.LF_MAX_FRAMES + 1) == -8
     assert L.lf_pool_keys(ctypes.byref(g), None, None, 1, p, p, None) == -1
+
+
+def test_backward_validation():
+    w = I.WAN480P_CHUNK
+    L = lf.lib()
+    p = ctypes.c_void_p(4096)
+    sp = I.rotated_slots(w).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def call(g, scale=1.0, dv=p, max_sel=30):
+        return L.lf_block_sparse_attn_bwd(ctypes.byref(g), p, p, p, sp, p, p, max_sel, ctypes.c_float(scale), p, p, p,
+                                          p, p, p, dv, None)
+
+    g = lf.geom_of(w)
+    assert call(g, scale=0.0) == -8
+    assert call(g, dv=None) == -1
+    assert call(g, max_sel=lf.LF_MAX_SEL + 1) == -4
+    g32 = lf.geom_of(w)
+    g32.dtype = 0  # float32 inputs: the backward takes bf16 only
+    assert call(g32) == -3
