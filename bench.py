@@ -47,6 +47,8 @@ def parse():
                     help="step: compress + select + attention every step (every hot-path row); fused: keys pooled "
                          "once on commit, then fused query pooling + selection and attention per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time lf_block_sparse_attn_bwd (bf16) and report it under 'backward'")
     ap.add_argument("--cpu-sample-qblocks", type=int, default=0, help="0: every query block (the whole call)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one elementwise kernel that reads and writes this many MiB "
@@ -314,6 +316,45 @@ def main():
         torch.neg(src, out=dst)  # reads and writes exactly n bf16 values
         torch.cuda.synchronize()
         result["calibration_copy_bytes_each_way"] = n * 2
+    if args.backward and w.dtype == "bf16":
+        # Backward of the same attention calls: out/lse from one forward per input set,
+        # then `steps` timed backward launches (HIP events on the launch stream).
+        # Algorithmic work: dV, dP, dQ and dK products, 8*d flops per visible
+        # (query, key) pair = twice the forward's effective FLOPs.
+        bw = []
+        fb = lf.Buffers(g, w.k_frames, w.k_blocks, with_lse=True)
+        for i, (q, kc, vc) in enumerate(sets):
+            lf.hsa_attention(g, q, kc, vc, slots, fb, scale)
+            o = fb.out.clone()
+            ls = fb.lse.clone()
+            gen = torch.Generator(device="cuda").manual_seed(100 + i)
+            do = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+            bw.append((o, ls, do, fb.sel_blocks.clone(), fb.n_sel.clone()))
+        delta = torch.empty(sets[0][0].shape[:3], dtype=torch.float32, device="cuda")
+        dq = torch.empty(sets[0][0].shape, dtype=torch.float32, device="cuda")
+        dk = torch.empty(sets[0][1].shape, dtype=torch.float32, device="cuda")
+        dv = torch.empty(sets[0][1].shape, dtype=torch.float32, device="cuda")
+
+        def bwd(i):
+            q, kc, vc = sets[i % N_SETS]
+            o, ls, do, sb, nsl = bw[i % N_SETS]
+            lf.lf_block_sparse_attn_bwd(g, q, kc, vc, slots, sb, nsl, scale, o, ls, do, delta, dq, dk, dv, stream)
+
+        for i in range(args.warmup):
+            bwd(i)
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        torch.cuda.synchronize()
+        for i in range(K):
+            bev[i][0].record(stream)
+            bwd(i)
+            bev[i][1].record(stream)
+        torch.cuda.synchronize()
+        bms = float(np.mean([e[0].elapsed_time(e[1]) for e in bev]))
+        bflops = 2.0 * flops_mean
+        result["backward"] = {"ms_per_call": round(bms, 4), "algorithmic_flops": bflops,
+                              "achieved": round(bflops / (bms * 1e-3) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
+                              "frac": round(bflops / (bms * 1e-3) / 1e12 / peak, 4),
+                              "kernels": "bwd_dq_kernel + bwd_dkv_kernel (dV pass, dK pass)"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, host0, w.k_frames, w.k_blocks, args.cpu_sample_qblocks)

@@ -40,15 +40,24 @@ struct BwdShape {
 };
 
 // Rows [0, count) of a row-major [*, D] bf16 matrix into LDS at pitch RS;
-// rows [count, rows) become zeros. All threads of the workgroup take part.
-template <int D>
-__device__ inline void stage_rows(char* lds, const __bf16* src, int count, int rows, int tid, int nthreads) {
+// rows [count, ROWS) become zeros. All NT threads of the workgroup take
+// part; each issues all its 16-byte loads before its first LDS store, so the
+// loads are in flight together.
+template <int D, int ROWS, int NT>
+__device__ inline void stage_rows(char* lds, const __bf16* src, int count, int tid) {
   using S = BwdShape<D>;
-  for (int i = tid; i < rows * S::CPR; i += nthreads) {
-    const int r = i / S::CPR, c = i - r * S::CPR;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r < count) v = *reinterpret_cast<const uint4*>(src + (int64_t)r * D + c * 8);
-    *reinterpret_cast<uint4*>(lds + r * S::RS + c * 16) = v;
+  constexpr int TOTAL = ROWS * S::CPR, N = (TOTAL + NT - 1) / NT;
+  uint4 v[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int i = tid + u * NT, r = i / S::CPR, c = i - r * S::CPR;
+    v[u] = i < TOTAL && r < count ? *reinterpret_cast<const uint4*>(src + (int64_t)r * D + c * 8)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int i = tid + u * NT, r = i / S::CPR, c = i - r * S::CPR;
+    if (i < TOTAL) *reinterpret_cast<uint4*>(lds + r * S::RS + c * 16) = v[u];
   }
 }
 
@@ -166,8 +175,8 @@ __global__ __launch_bounds__(64 * WPQ) void bwd_dq_kernel(const __bf16* __restri
     }
     const int64_t base = ((bh * g.S + slot) * (int64_t)g.T + start) * D;
     __syncthreads();  // the previous tile's reads are done
-    stage_rows<D>(ks, kc + base, count, 64, tid, NT);
-    stage_rows<D>(vs, vc + base, count, 64, tid, NT);
+    stage_rows<D, 64, NT>(ks, kc + base, count, tid);
+    stage_rows<D, 64, NT>(vs, vc + base, count, tid);
     __syncthreads();
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
@@ -289,8 +298,8 @@ __global__ __launch_bounds__(128) void bwd_dkv_kernel(const __bf16* __restrict__
       const int nrows = min(g.b, g.T - jq * g.b);
       const int64_t row0 = bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b;
       const int halves = (nrows + 31) / 32;
-      stage_rows<D>(qs, q + row0 * D, nrows, 32 * halves, tid, NT);
-      stage_rows<D>(gs, dout + row0 * D, nrows, 32 * halves, tid, NT);
+      stage_rows<D, MAXQ, NT>(qs, q + row0 * D, nrows, tid);
+      stage_rows<D, MAXQ, NT>(gs, dout + row0 * D, nrows, tid);
       for (int r = tid; r < 32 * halves; r += NT) {
         lse2s[r] = r < nrows ? lse[row0 + r] * kLog2e : INFINITY;  // +inf: P = 0 on missing rows
         if constexpr (DK) dds[r] = r < nrows ? delta[row0 + r] : 0.0f;
