@@ -63,16 +63,6 @@ struct Mma<float> {
   }
 };
 
-// A wave-uniform pointer moved to scalar registers (so address arithmetic on
-// it stays scalar and loads can use the scalar-base form).
-template <typename P>
-__device__ inline P* uniform_ptr(P* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
-}
-
 // Pins a computed value at this point of the program: an empty asm that
 // claims to modify the register, so no optimisation pass moves the
 // computation past it (the scheduling fences alone bind only the final
@@ -92,8 +82,6 @@ __device__ inline float pin(float x) {
 template <typename T, int WPQ>
 constexpr int WAVES_PER_SIMD = sizeof(T) == 2 && WPQ > 1 ? 2 : 1;
 
-// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 only.
-constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
 // One workgroup's walk: per-wavefront query fragments and accumulators, the
 // scalar tile producer, the LDS loader and the per-tile math.

@@ -39,27 +39,48 @@ struct BwdShape {
   static constexpr int DB = D / 32;       // 32-column blocks of d
 };
 
-// Rows [0, count) of a row-major [*, D] bf16 matrix into LDS at pitch RS;
-// rows [count, ROWS) become zeros. All NT threads of the workgroup take
-// part; each issues all its 16-byte loads before its first LDS store, so the
-// loads are in flight together.
+// Direct HBM -> LDS loads of a tile of ROWS rows (buffer loads that write
+// LDS, 16 bytes per lane, no registers). Load instruction i of wavefront w
+// fills 64 consecutive 16-byte LDS slots; slot s holds chunk s mod SPR of
+// row s / SPR, and the pad slots of a row re-read a chunk of the same row
+// (same cache line). The buffer resource spans the tile's `count` valid rows,
+// so rows past it come back as zeros and no load leaves the matrix.
 template <int D, int ROWS, int NT>
-__device__ inline void stage_rows(char* lds, const __bf16* src, int count, int tid) {
-  using S = BwdShape<D>;
-  constexpr int TOTAL = ROWS * S::CPR, N = (TOTAL + NT - 1) / NT;
-  uint4 v[N];
+struct TileDma {
+  static constexpr int RS = BwdShape<D>::RS, CPR = BwdShape<D>::CPR, SPR = RS / 16;
+  static constexpr int SLOTS = ROWS * SPR, NI = (SLOTS + NT - 1) / NT;
+  static_assert(SLOTS % 64 == 0, "whole load instructions");
+  uint32_t off[NI];
+  __device__ inline void init(int tid) {
+    const int wv = tid >> 6, lane = tid & 63;
 #pragma unroll
-  for (int u = 0; u < N; ++u) {
-    const int i = tid + u * NT, r = i / S::CPR, c = i - r * S::CPR;
-    v[u] = i < TOTAL && r < count ? *reinterpret_cast<const uint4*>(src + (int64_t)r * D + c * 8)
-                                  : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < NI; ++i) {
+      const int slot = (i * (NT / 64) + wv) * 64 + lane;
+      const int row = min(slot / SPR, ROWS - 1);
+      int c = slot - (slot / SPR) * SPR;
+      while (c >= CPR) c -= CPR;
+      off[i] = (uint32_t)(row * D * 2 + c * 16);
+    }
   }
+  __device__ inline void issue(char* lds, const __bf16* src, int count, int tid) const {
+#if defined(__HIP_DEVICE_COMPILE__)  // (the builtin exists only for the device pass)
+    const int wv = tid >> 6;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(uniform_ptr(src)), (short)0, count * D * 2, kRawBufferFlags);
 #pragma unroll
-  for (int u = 0; u < N; ++u) {
-    const int i = tid + u * NT, r = i / S::CPR, c = i - r * S::CPR;
-    if (i < TOTAL) *reinterpret_cast<uint4*>(lds + r * S::RS + c * 16) = v[u];
+    for (int i = 0; i < NI; ++i) {
+      const int L0 = (i * (NT / 64) + wv) * 64;
+      if ((i + 1) * NT <= SLOTS || L0 < SLOTS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds + L0 * 16), 16, off[i], 0, 0, 0);
+    }
+#else
+    (void)lds;
+    (void)src;
+    (void)count;
+    (void)tid;
+#endif
   }
-}
+};
 
 // MFMA operand fragments (lane l, l32 = l % 32, h = l / 32):
 // rows r0 + l32 of an LDS tile, d = 16t + 8h .. +7 (A operand, rows = M).
@@ -99,6 +120,69 @@ __device__ inline void store_acc_t(float* dst, const f32x16& acc, int db, int h,
   }
 }
 
+// Tile t of a query block's walk, from index t on: the current chunk's
+// 64-key tiles, then the tiles of its selected history blocks (ignored ids
+// skipped). On return t is the tile found; false when the walk is over.
+__device__ inline bool dq_tile(const KGeom& g, const int32_t* sel, int64_t item, int max_sel, int tpf, int n_cur,
+                               int hpb, int64_t bh, int& t, int n_tiles, int64_t& base, int& count) {
+  for (; t < n_tiles; ++t) {
+    int slot, start;
+    if (t < n_cur) {
+      const int f2 = t / tpf, tt = t - f2 * tpf;
+      slot = g.slot[g.Fh + f2];
+      start = tt * 64;
+      count = min(64, g.T - start);
+    } else {
+      const int e = (t - n_cur) / hpb, half = (t - n_cur) - e * hpb;
+      const int x = sel[item * max_sel + e];
+      if (x < 0 || x >= g.Fh * g.nb) continue;  // ignored id
+      const int f = x / g.nb, jb = x - f * g.nb;
+      slot = g.slot[f];
+      start = jb * g.b + half * 64;
+      count = min(64, min(jb * g.b + g.b, g.T) - start);
+      if (count <= 0) continue;
+    }
+    base = ((bh * g.S + slot) * (int64_t)g.T + start) * g.D;
+    return true;
+  }
+  return false;
+}
+
+// One tile of the dQ walk on the stage (ks, vs), `count` valid keys.
+template <int D>
+__device__ inline void dq_tile_math(const char* ks, const char* vs, int count, const bf16x8* qf, const bf16x8* dof,
+                                    f32x16* acc, float c2, float lse2, float dd, int lane) {
+  using S = BwdShape<D>;
+  const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.0f;
+      dp[r] = 0.0f;
+    }
+#pragma unroll
+    for (int st = 0; st < S::QSTEPS; ++st) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(ks, 32 * kh, st, l32, h), qf[st], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vs, 32 * kh, st, l32, h), dof[st], dp, 0, 0, 0);
+    }
+    bf16x8 b0, b1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool kv = 32 * kh + acc_row(r, h) < count;
+      const float p = kv ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2)) : 0.0f;
+      const __bf16 d = (__bf16)(p * (dp[r] - dd));
+      if (r < 8) b0[r] = d; else b1[r - 8] = d;
+    }
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) {
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ks, 2 * kh, db, lane), b0, acc[db], 0, 0, 0);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ks, 2 * kh + 1, db, lane), b1, acc[db], 0, 0, 0);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dQ (and D_i): one workgroup of WPQ wavefronts per (batch, head, query block).
 template <int D, int WPQ>
@@ -111,8 +195,12 @@ __global__ __launch_bounds__(64 * WPQ) void bwd_dq_kernel(const __bf16* __restri
                                                           float* __restrict__ dq) {
   using S = BwdShape<D>;
   constexpr int NT = 64 * WPQ;
-  __shared__ __attribute__((aligned(16))) char ks[64 * S::RS];
-  __shared__ __attribute__((aligned(16))) char vs[64 * S::RS];
+  // Double-buffered K/V stages, separate arrays so the compiler sees that the
+  // fragment reads of one stage never wait on the loads filling the other.
+  __shared__ __attribute__((aligned(1024))) char ks0[64 * S::RS];
+  __shared__ __attribute__((aligned(1024))) char vs0[64 * S::RS];
+  __shared__ __attribute__((aligned(1024))) char ks1[64 * S::RS];
+  __shared__ __attribute__((aligned(1024))) char vs1[64 * S::RS];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -155,99 +243,144 @@ __global__ __launch_bounds__(64 * WPQ) void bwd_dq_kernel(const __bf16* __restri
   const int n_cur = g.Fc * tpf;
   const int hpb = g.b > 64 ? 2 : 1;
   const int len = max_sel > 0 ? min(max(nsel[item], 0), max_sel) : 0;
-  const int n_hist_blocks = g.Fh * g.nb;
-  for (int t = 0; t < n_cur + len * hpb; ++t) {
-    int slot, start, count;
-    if (t < n_cur) {
-      const int f2 = t / tpf, tt = t - f2 * tpf;
-      slot = g.slot[g.Fh + f2];
-      start = tt * 64;
-      count = min(64, g.T - start);
-    } else {
-      const int e = (t - n_cur) / hpb, half = (t - n_cur) - e * hpb;
-      const int x = sel[item * max_sel + e];
-      if (x < 0 || x >= n_hist_blocks) continue;  // ignored id (uniform: every wavefront skips it)
-      const int f = x / g.nb, jb = x - f * g.nb;
-      slot = g.slot[f];
-      start = jb * g.b + half * 64;
-      count = min(64, min(jb * g.b + g.b, g.T) - start);
-      if (count <= 0) continue;
-    }
-    const int64_t base = ((bh * g.S + slot) * (int64_t)g.T + start) * D;
-    __syncthreads();  // the previous tile's reads are done
-    stage_rows<D, 64, NT>(ks, kc + base, count, tid);
-    stage_rows<D, 64, NT>(vs, vc + base, count, tid);
-    __syncthreads();
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.0f;
-        dp[r] = 0.0f;
-      }
-#pragma unroll
-      for (int st = 0; st < S::QSTEPS; ++st) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(ks, 32 * kh, st, l32, h), qf[st], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vs, 32 * kh, st, l32, h), dof[st], dp, 0, 0, 0);
-      }
-      bf16x8 b0, b1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool kv = 32 * kh + acc_row(r, h) < count;
-        const float p = kv ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2)) : 0.0f;
-        const __bf16 d = (__bf16)(p * (dp[r] - dd));
-        if (r < 8) b0[r] = d; else b1[r - 8] = d;
-      }
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db) {
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ks, 2 * kh, db, lane), b0, acc[db], 0, 0, 0);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ks, 2 * kh + 1, db, lane), b1, acc[db], 0, 0, 0);
-      }
-    }
+  const int n_tiles = n_cur + len * hpb;
+  TileDma<D, 64, NT> dma;
+  dma.init(tid);
+  int t = 0, count = 0, ncount = 0;
+  int64_t nbase = 0;
+  bool have = dq_tile(g, sel, item, max_sel, tpf, n_cur, hpb, bh, t, n_tiles, nbase, ncount);
+  if (have) {
+    dma.issue(ks0, kc + nbase, ncount, tid);
+    dma.issue(vs0, vc + nbase, ncount, tid);
   }
+  // Per tile: wait for its loads, barrier (everyone's landed; everyone is done
+  // with the other stage), start the next tile's loads into the other stage,
+  // compute. Unrolled by two so each half names its stage buffers.
+#define LF_DQ_STEP(KA, VA, KB, VB)                                                         \
+  {                                                                                      \
+    count = ncount;                                                                      \
+    ++t;                                                                                 \
+    const bool more = dq_tile(g, sel, item, max_sel, tpf, n_cur, hpb, bh, t, n_tiles, nbase, ncount); \
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);                                                \
+    __syncthreads();                                                                     \
+    if (more) {                                                                          \
+      dma.issue(KB, kc + nbase, ncount, tid);                                            \
+      dma.issue(VB, vc + nbase, ncount, tid);                                            \
+    }                                                                                    \
+    dq_tile_math<D>(KA, VA, count, qf, dof, acc, c2, lse2, dd, lane);                    \
+    have = more;                                                                         \
+  }
+  while (have) {
+    LF_DQ_STEP(ks0, vs0, ks1, vs1)
+    if (!have) break;
+    LF_DQ_STEP(ks1, vs1, ks0, vs0)
+  }
+#undef LF_DQ_STEP
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no load may still be writing LDS when the workgroup ends
   if (!ok) return;
   float* dst = dq + (row0 + qr) * D;
 #pragma unroll
   for (int db = 0; db < S::DB; ++db) store_acc_t(dst, acc[db], db, h, scale);
 }
 
+// One query block against this wavefront's 32 keys (K^T, V^T in registers):
+// per 32 query rows, S = Q K^T and P; dV^T += dO^T P, or dP = dO V^T,
+// dS = P (dP - D) and dK^T += Q^T dS. ls holds lse*log2(e) per row (+inf on
+// missing rows, so their P is 0), dd the row's D.
+template <int D, int MODE>  // MODE: 0 dV, 1 dK, 2 both (acc = dV, acc2 = dK)
+__device__ inline void dkv_block_math(const char* qs, const char* gs, const float* ls, const float* dd, int nrows,
+                                      const bf16x8* kf, const bf16x8* vf, f32x16* acc, f32x16* acc2, float c2,
+                                      bool kok, int lane) {
+  using S = BwdShape<D>;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int halves = (nrows + 31) / 32;
+  for (int qh = 0; qh < halves; ++qh) {
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+    for (int st = 0; st < S::QSTEPS; ++st)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qs, 32 * qh, st, l32, h), kf[st], s, 0, 0, 0);
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      p[r] = kok ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -ls[32 * qh + acc_row(r, h)])) : 0.0f;
+    if constexpr (MODE != 1) {  // dV^T += dO^T P
+      bf16x8 b0, b1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (r < 8) b0[r] = (__bf16)p[r]; else b1[r - 8] = (__bf16)p[r];
+      }
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) {
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh, db, lane), b0, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh + 1, db, lane), b1, acc[db], 0, 0, 0);
+      }
+    }
+    if constexpr (MODE != 0) {  // dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
+      f32x16* ak = MODE == 2 ? acc2 : acc;
+      f32x16 dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = 0.0f;
+#pragma unroll
+      for (int st = 0; st < S::QSTEPS; ++st)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(gs, 32 * qh, st, l32, h), vf[st], dp, 0, 0, 0);
+      bf16x8 b0, b1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const __bf16 d = (__bf16)(p[r] * (dp[r] - dd[32 * qh + acc_row(r, h)]));
+        if (r < 8) b0[r] = d; else b1[r - 8] = d;
+      }
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) {
+        ak[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qs, 2 * qh, db, lane), b0, ak[db], 0, 0, 0);
+        ak[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qs, 2 * qh + 1, db, lane), b1, ak[db], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dK (DK) or dV: one workgroup of two wavefronts per key tile of one (batch,
 // head). Tiles per (batch, head): the current chunk's Fc * ceil(T/64) tiles,
 // then every history block's tile(s) (blocks of more than 64 keys are two).
-template <int D, int MAXQ, bool DK>
-__global__ __launch_bounds__(128) void bwd_dkv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
+template <int D, int MAXQ, int MODE, int NW, bool CUR>
+__global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void bwd_dkv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                                                       const __bf16* __restrict__ vc, const __bf16* __restrict__ dout,
                                                       const float* __restrict__ lse, const float* __restrict__ delta,
                                                       const int32_t* __restrict__ sel,
                                                       const int32_t* __restrict__ nsel, int max_sel, float scale,
-                                                      const KGeom g, float* __restrict__ dst) {
+                                                      const KGeom g, float* __restrict__ dst,
+                                                      float* __restrict__ dst2) {
+  constexpr bool DK = MODE != 0;  // needs V^T and D
   using S = BwdShape<D>;
-  constexpr int NT = 128;
-  __shared__ __attribute__((aligned(16))) char qs[MAXQ * S::RS];
-  __shared__ __attribute__((aligned(16))) char gs[MAXQ * S::RS];
-  __shared__ float lse2s[MAXQ];
-  __shared__ float dds[MAXQ];
-  __shared__ int qlist[64];
+  constexpr int NT = 64 * NW;
+  constexpr int KEYS = 32 * NW;  // keys per workgroup
+  constexpr int QCAP = 1024;     // query blocks listed per batch
+  __shared__ __attribute__((aligned(1024))) char qs0[MAXQ * S::RS];
+  __shared__ __attribute__((aligned(1024))) char gs0[MAXQ * S::RS];
+  __shared__ __attribute__((aligned(1024))) char qs1[MAXQ * S::RS];
+  __shared__ __attribute__((aligned(1024))) char gs1[MAXQ * S::RS];
+  __shared__ float ls0[MAXQ], ls1[MAXQ], ds0[MAXQ], ds1[MAXQ];
+  __shared__ int qlist[QCAP];
   __shared__ int qcount;
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tpf = (g.T + 63) / 64;
-  const int n_cur = g.Fc * tpf;
   const int hpb = g.b > 64 ? 2 : 1;
-  const int per_bh = n_cur + g.Fh * g.nb * hpb;
+  const int gpf = (g.T + KEYS - 1) / KEYS;  // key groups per current frame
+  const int per_bh = CUR ? g.Fc * gpf : g.Fh * g.nb * hpb;
   const int64_t bh = blockIdx.x / per_bh;
   const int ti = (int)(blockIdx.x - bh * per_bh);
   int f, start, count, hist_id = -1;
-  if (ti < n_cur) {
-    const int f2 = ti / tpf;
+  if constexpr (CUR) {
+    const int f2 = ti / gpf;
     f = g.Fh + f2;
-    start = (ti - f2 * tpf) * 64;
-    count = min(64, g.T - start);
+    start = (ti - f2 * gpf) * KEYS;
+    count = min(KEYS, g.T - start);
   } else {
-    const int hi = ti - n_cur;
+    static_assert(KEYS == 64, "a history workgroup holds one 64-key tile");
+    const int hi = ti;
     f = hi / (g.nb * hpb);
     const int rem = hi - f * g.nb * hpb;
     const int jb = rem / hpb, half = rem - jb * hpb;
@@ -267,88 +400,107 @@ __global__ __launch_bounds__(128) void bwd_dkv_kernel(const __bf16* __restrict__
     kf[t] = own_frag(kc + (krow0 + (kok ? key : 0)) * D, kok, t, h);
     if constexpr (DK) vf[t] = own_frag(vc + (krow0 + (kok ? key : 0)) * D, kok, t, h);
   }
-  f32x16 acc[S::DB];
+  f32x16 acc[S::DB], acc2[MODE == 2 ? S::DB : 1];
 #pragma unroll
   for (int db = 0; db < S::DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  if constexpr (MODE == 2) {
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc2[db][r] = 0.0f;
+  }
+  TileDma<D, MAXQ, NT> dma;
+  dma.init(tid);
 
-  // Query blocks that see this tile, 64 candidates at a time.
-  for (int c0 = 0; c0 < g.nqb; c0 += 64) {
-    __syncthreads();  // every wavefront has read the previous batch's list and count
+  for (int c0 = 0; c0 < g.nqb; c0 += QCAP) {
+    // The query blocks in [c0, c0 + QCAP) that see this tile, ascending.
+    __syncthreads();  // the previous batch's list is consumed
     if (wv == 0) {
-      const int qb = c0 + lane;
-      bool sees = qb < g.nqb;
-      if (sees && hist_id >= 0) {
-        const int64_t item = bh * g.nqb + qb;
-        const int len = max_sel > 0 ? min(max(nsel[item], 0), max_sel) : 0;
-        bool found = false;
-        for (int e = 0; e < len; ++e) found = found || sel[item * max_sel + e] == hist_id;
-        sees = found;
+      int n = 0;
+      for (int k0 = c0; k0 < min(c0 + QCAP, g.nqb); k0 += 64) {
+        const int qb = k0 + lane;
+        bool sees = qb < min(c0 + QCAP, g.nqb);
+        if (sees && hist_id >= 0) {
+          const int64_t item = bh * g.nqb + qb;
+          const int len = max_sel > 0 ? min(max(nsel[item], 0), max_sel) : 0;
+          bool found = false;
+          for (int e = 0; e < len; ++e) found = found || sel[item * max_sel + e] == hist_id;
+          sees = found;
+        }
+        const uint64_t m = __builtin_amdgcn_ballot_w64(sees);
+        if (sees) qlist[n + __builtin_popcountll(m & ((1ull << lane) - 1ull))] = qb;
+        n += __builtin_popcountll(m);
       }
-      const uint64_t m = __builtin_amdgcn_ballot_w64(sees);
-      if (sees) qlist[__builtin_popcountll(m & ((1ull << lane) - 1ull))] = qb;
-      if (lane == 0) qcount = __builtin_popcountll(m);
+      if (lane == 0) qcount = n;
     }
     __syncthreads();
     const int nq = qcount;
-    for (int i = 0; i < nq; ++i) {
-      const int qb = qlist[i];
+    if (nq == 0) continue;
+    // Stage the first query block; then per block: wait, barrier, start the
+    // next block's loads into the other stage, compute, and write the next
+    // block's lse / delta rows (loaded before its tiles, so already here).
+    int i = 0, nrows = 0;
+    int64_t row0 = 0;
+    {
+      const int qb = qlist[0];
       const int fc = qb / g.nb, jq = qb - fc * g.nb;
-      const int nrows = min(g.b, g.T - jq * g.b);
-      const int64_t row0 = bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b;
-      const int halves = (nrows + 31) / 32;
-      stage_rows<D, MAXQ, NT>(qs, q + row0 * D, nrows, tid);
-      stage_rows<D, MAXQ, NT>(gs, dout + row0 * D, nrows, tid);
-      for (int r = tid; r < 32 * halves; r += NT) {
-        lse2s[r] = r < nrows ? lse[row0 + r] * kLog2e : INFINITY;  // +inf: P = 0 on missing rows
-        if constexpr (DK) dds[r] = r < nrows ? delta[row0 + r] : 0.0f;
+      nrows = min(g.b, g.T - jq * g.b);
+      row0 = bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b;
+      if (tid < MAXQ) {
+        ls0[tid] = tid < nrows ? lse[row0 + tid] * kLog2e : INFINITY;  // +inf: P = 0 on missing rows
+        if constexpr (DK) ds0[tid] = tid < nrows ? delta[row0 + tid] : 0.0f;
       }
-      __syncthreads();
-      for (int qh = 0; qh < halves; ++qh) {
-        f32x16 s;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-#pragma unroll
-        for (int st = 0; st < S::QSTEPS; ++st)
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qs, 32 * qh, st, l32, h), kf[st], s, 0, 0, 0);
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          p[r] = kok ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2s[32 * qh + acc_row(r, h)])) : 0.0f;
-        bf16x8 b0, b1;
-        if constexpr (DK) {
-          f32x16 dp;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) dp[r] = 0.0f;
-#pragma unroll
-          for (int st = 0; st < S::QSTEPS; ++st)
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(gs, 32 * qh, st, l32, h), vf[st], dp, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const __bf16 d = (__bf16)(p[r] * (dp[r] - dds[32 * qh + acc_row(r, h)]));
-            if (r < 8) b0[r] = d; else b1[r - 8] = d;
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if (r < 8) b0[r] = (__bf16)p[r]; else b1[r - 8] = (__bf16)p[r];
-          }
-        }
-        const char* at = DK ? qs : gs;  // dK^T += Q^T dS; dV^T += dO^T P
-#pragma unroll
-        for (int db = 0; db < S::DB; ++db) {
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(at, 2 * qh, db, lane), b0, acc[db], 0, 0, 0);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(at, 2 * qh + 1, db, lane), b1, acc[db], 0, 0, 0);
-        }
-      }
-      __syncthreads();  // the staged rows are rewritten by the next query block
+      dma.issue(qs0, q + row0 * D, nrows, tid);
+      dma.issue(gs0, dout + row0 * D, nrows, tid);
     }
+#define LF_DKV_STEP(QA, GA, LA, DA, QB, GB, LB, DB_)                                          \
+  {                                                                                         \
+    const int cur_rows = nrows;                                                             \
+    const bool more = i + 1 < nq;                                                           \
+    float nl = 0.0f, nd = 0.0f;                                                             \
+    if (more) {                                                                             \
+      const int qb = qlist[i + 1];                                                          \
+      const int fc = qb / g.nb, jq = qb - fc * g.nb;                                        \
+      nrows = min(g.b, g.T - jq * g.b);                                                     \
+      row0 = bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b;                             \
+      if (tid < nrows) {                                                                    \
+        nl = lse[row0 + tid];                                                               \
+        if constexpr (DK) nd = delta[row0 + tid];                                           \
+      }                                                                                     \
+    }                                                                                       \
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);                                                   \
+    __syncthreads();                                                                        \
+    if (more) {                                                                             \
+      dma.issue(QB, q + row0 * D, nrows, tid);                                              \
+      dma.issue(GB, dout + row0 * D, nrows, tid);                                           \
+    }                                                                                       \
+    dkv_block_math<D, MODE>(QA, GA, LA, DA, cur_rows, kf, vf, acc, acc2, c2, kok, lane);    \
+    if (more && tid < MAXQ) {                                                               \
+      LB[tid] = tid < nrows ? nl * kLog2e : INFINITY;                                       \
+      if constexpr (DK) DB_[tid] = nd;                                                      \
+    }                                                                                       \
+    ++i;                                                                                    \
   }
+    while (i < nq) {
+      LF_DKV_STEP(qs0, gs0, ls0, ds0, qs1, gs1, ls1, ds1)
+      if (i >= nq) break;
+      LF_DKV_STEP(qs1, gs1, ls1, ds1, qs0, gs0, ls0, ds0)
+    }
+#undef LF_DKV_STEP
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no load may still be writing LDS when the workgroup ends
   if (!kok) return;
+  // MODE 0: dst = dV; MODE 1: dst = dK; MODE 2: dst = dV, dst2 = dK.
   float* row = dst + (krow0 + key) * D;
 #pragma unroll
-  for (int db = 0; db < S::DB; ++db) store_acc_t(row, acc[db], db, h, DK ? scale : 1.0f);
+  for (int db = 0; db < S::DB; ++db) store_acc_t(row, acc[db], db, h, MODE == 1 ? scale : 1.0f);
+  if constexpr (MODE == 2) {
+    float* row2 = dst2 + (krow0 + key) * D;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) store_acc_t(row2, acc2[db], db, h, scale);
+  }
 }
 
 template <int D>
@@ -379,19 +531,29 @@ hipError_t launch_bwd_d(const KGeom& g, const void* q, const void* k, const void
                          max_sel, scale, g, delta, dq);
       break;
   }
-  const int tpf = (g.T + 63) / 64;
-  const unsigned nk = (unsigned)((int64_t)g.B * g.H * (g.Fc * tpf + g.Fh * g.nb * (g.b > 64 ? 2 : 1)));
+  // Current-chunk keys are seen by every query block of the head: 256 keys
+  // per workgroup (eight wavefronts) so each staged query block feeds four
+  // times the MFMA work. History blocks have their own query blocks: one
+  // 64-key tile per workgroup.
+  const unsigned ncur = (unsigned)((int64_t)g.B * g.H * g.Fc * ((g.T + 255) / 256));
+  const unsigned nhist = (unsigned)((int64_t)g.B * g.H * g.Fh * g.nb * (g.b > 64 ? 2 : 1));
+  // (History workgroups are held to one wavefront per SIMD by their LDS, so
+  // they take dK and dV in one pass; the current-chunk passes run two
+  // wavefronts per SIMD and keep dK and dV apart to fit 256 registers.)
+#define LF_DKV(MAXQ)                                                                                                   \
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, MAXQ, 0, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta,  \
+                     sel, nsel, max_sel, scale, g, dv, nullptr);                                                       \
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, MAXQ, 1, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta,  \
+                     sel, nsel, max_sel, scale, g, dk, nullptr);                                                       \
+  if (nhist > 0)                                                                                                       \
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, MAXQ, 2, 2, false>), dim3(nhist), dim3(128), 0, stream, Q, K, V, G, lse,    \
+                       delta, sel, nsel, max_sel, scale, g, dv, dk);
   if (g.b <= 64) {
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 64, false>), dim3(nk), dim3(128), 0, stream, Q, K, V, G, lse, delta, sel,
-                       nsel, max_sel, scale, g, dv);
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 64, true>), dim3(nk), dim3(128), 0, stream, Q, K, V, G, lse, delta, sel,
-                       nsel, max_sel, scale, g, dk);
+    LF_DKV(64)
   } else {
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 128, false>), dim3(nk), dim3(128), 0, stream, Q, K, V, G, lse, delta, sel,
-                       nsel, max_sel, scale, g, dv);
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 128, true>), dim3(nk), dim3(128), 0, stream, Q, K, V, G, lse, delta, sel,
-                       nsel, max_sel, scale, g, dk);
+    LF_DKV(128)
   }
+#undef LF_DKV
   return hipGetLastError();
 }
 

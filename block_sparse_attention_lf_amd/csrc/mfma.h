@@ -19,4 +19,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 // output: 8*(r/4) + 4*h + r%4 (the column is the lane index mod 32).
 __device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 only.
+constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
+
+// Buffer resource word 3 for raw (untyped) dword access on this GPU family.
+constexpr int kRawBufferFlags = 0x00020000;
+
+// A wave-uniform pointer moved to scalar registers (so address arithmetic on
+// it stays scalar and loads can use the scalar-base form).
+template <typename P>
+__device__ inline P* uniform_ptr(P* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+
 }  // namespace lf
