@@ -196,6 +196,32 @@ def _finish(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# FP8 inputs: OCP E4M3 codes with an OCP MX (E8M0) scale per 32 channels
+# --------------------------------------------------------------------------
+
+def mx_quantize(x: np.ndarray, block: int = 32):
+    """Quantise float values to E4M3 codes with one E8M0 scale per ``block``
+    consecutive channels of the last axis: the shared exponent of a block is
+    the smallest one with max |x| / 2^exp <= 448 (E4M3's largest value, so no
+    element clips), elements are x / 2^exp rounded to nearest-even E4M3. An
+    all-zero block gets scale 2^-127. Returns (codes uint8 [..., D], scales uint8 [..., D/block]).
+    (Input preparation for the FP8 variant; the kernel and the oracle only
+    read the codes.)
+    """
+    import torch  # float8_e4m3fn gives nearest-even rounding of the scaled values
+
+    x = np.asarray(x, np.float32)
+    D = x.shape[-1]
+    xb = x.reshape(x.shape[:-1] + (D // block, block)).astype(np.float64)
+    amax = np.max(np.abs(xb), axis=-1)
+    exp = np.where(amax > 0, np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / 448.0)), -127).astype(np.int64)
+    exp = np.clip(exp, -127, 127)
+    y = np.clip(xb / np.exp2(exp)[..., None], -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes.reshape(x.shape).copy(), (exp + 127).astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
 # Cache slot tables (which physical slot holds which logical frame)
 # --------------------------------------------------------------------------
 

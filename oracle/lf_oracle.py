@@ -36,7 +36,11 @@ Readings where the pages leave a step open (each restated at its function):
   R18 the single-level ("1D") ablation variant ranks all non-sink history
       blocks in one top-k;
   R19 the backward pass is the gradient of the loss sum(out * dout) through
-      the same masks (the selection itself is not differentiated).
+      the same masks (the selection itself is not differentiated);
+  R20 the FP8 variant takes queries and keys as OCP E4M3 codes with one OCP
+      MX (E8M0) scale per 32 consecutive channels of each token (per-token
+      activation scaling, in the form the matrix cores apply); values and
+      P stay bf16.
 Pooling sums in float64 and rounds the mean once to float32; scores are
 float64 dot products of those float32 values; attention is float64 dense
 masked softmax.
@@ -375,6 +379,56 @@ def attention_grad(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, fram
                 dk_cache[b, h, frame_slot[f]] = dK[f * T:(f + 1) * T]
                 dv_cache[b, h, frame_slot[f]] = dV[f * T:(f + 1) * T]
     return {"dq": dq, "dk_cache": dk_cache, "dv_cache": dv_cache}
+
+
+# ---------------------------------------------------------------------------
+# FP8 inputs (reading R20): OCP 8-bit floating point E4M3 values with OCP
+# microscaling (MX) E8M0 scales, one per 32 consecutive channels of a token
+# ---------------------------------------------------------------------------
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Values of OCP E4M3 codes (the variant without infinities), float64.
+
+    Bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa. Exponent
+    field 0: subnormal, (m/8) * 2^-6; otherwise (1 + m/8) * 2^(e-7). The one
+    NaN pattern per sign is exponent 15 with mantissa 7; the largest finite
+    magnitude is 448 (exponent 15, mantissa 6).
+    Pinned by tests/test_oracle_fp8.py (printed values, torch's float8_e4m3fn).
+    """
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def e8m0_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP MX scale: 2^(code - 127); code 255 is NaN. Float64."""
+    c = np.asarray(codes, np.uint8).astype(np.float64)
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """x[..., d] = e4m3(codes[..., d]) * e8m0(scales[..., d // block]), float64.
+
+    codes [..., D] uint8, scales [..., D // block] uint8 (one per block of
+    consecutive channels of each token).
+    """
+    x = e4m3_decode(codes)
+    sc = np.repeat(e8m0_decode(scales), block, axis=-1)
+    return x * sc
+
+
+def attention_fp8(q8: np.ndarray, q_scale: np.ndarray, k8_cache: np.ndarray, k_scale: np.ndarray,
+                  v_cache: np.ndarray, frame_slot: Sequence[int], sel_blocks: np.ndarray, n_sel: np.ndarray,
+                  tokens_per_frame: int, block: int, chunk_frames: int, hist_frames: int, scale: float,
+                  qblocks=None) -> Dict[str, np.ndarray]:
+    """The block-sparse attention on MX-FP8 queries and keys: the exact values
+    the codes and scales stand for, then ``attention`` (float64)."""
+    return attention(mx_dequantize(q8, q_scale), mx_dequantize(k8_cache, k_scale), v_cache, frame_slot,
+                     sel_blocks, n_sel, tokens_per_frame, block, chunk_frames, hist_frames, scale, qblocks)
 
 
 # ---------------------------------------------------------------------------
