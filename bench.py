@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "effective attention TFLOP/s + % MFMA bf16 peak per 480p chunk; ms/chunk-layer"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 N_SETS = 4
@@ -49,6 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="also time lf_block_sparse_attn_bwd (bf16) and report it under 'backward'")
+    ap.add_argument("--fp8", action="store_true",
+                    help="also time lf_block_sparse_attn_fp8 (MX-FP8 q/k) on the same selections; report under 'fp8'")
     ap.add_argument("--cpu-sample-qblocks", type=int, default=0, help="0: every query block (the whole call)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one elementwise kernel that reads and writes this many MiB "
@@ -355,6 +358,44 @@ def main():
                               "achieved": round(bflops / (bms * 1e-3) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
                               "frac": round(bflops / (bms * 1e-3) / 1e12 / peak, 4),
                               "kernels": "bwd_dq_kernel + bwd_dkv_kernel (dV pass, dK pass)"}
+    if args.fp8 and w.dtype == "bf16" and w.head_dim == 128 and 32 < w.block <= 64:
+        # The same attention calls with queries and keys as MX-FP8 (E4M3 codes,
+        # one E8M0 scale per 32 channels, quantised on the host, untimed) and
+        # the bf16 step's selections. Score products run at the FP8 MFMA rate
+        # and PV products at the bf16 one: with equal FLOPs in each, the
+        # kernel's roofline is 1 / (0.5/P_fp8 + 0.5/P_bf16).
+        print("[bench] quantising the input sets to MX-FP8", file=sys.stderr, flush=True)
+        f8 = []
+        for i, (q, kc, vc) in enumerate(sets):
+            lf.hsa_attention(g, q, kc, vc, slots, bufs, scale)
+            q8, qs = I.mx_quantize(q.float().cpu().numpy())
+            k8, ks = I.mx_quantize(kc.float().cpu().numpy())
+            f8.append(tuple(torch.from_numpy(a).cuda() for a in (q8, qs, k8, ks)) +
+                      (bufs.sel_blocks.clone(), bufs.n_sel.clone()))
+        out8 = torch.empty_like(bufs.out)
+
+        def fwd8(i):
+            q8, qs, k8, ks, sb, nsl = f8[i % N_SETS]
+            lf.lf_block_sparse_attn_fp8(g, q8, qs, k8, ks, sets[i % N_SETS][2], slots, sb, nsl, scale, out8, None,
+                                        stream)
+
+        for i in range(args.warmup):
+            fwd8(i)
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        torch.cuda.synchronize()
+        for i in range(K):
+            fev[i][0].record(stream)
+            fwd8(i)
+            fev[i][1].record(stream)
+        torch.cuda.synchronize()
+        fms = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
+        fpeak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+        fach = flops_mean / (fms * 1e-3) / 1e12
+        result["fp8"] = {"ms_per_call": round(fms, 4), "algorithmic_flops": flops_mean, "achieved": round(fach, 2),
+                         "peak": round(fpeak, 1), "unit": "TFLOP/s", "frac": round(fach / fpeak, 4),
+                         "frac_of_bf16_peak": round(fach / PEAK_BF16_TFLOPS, 4),
+                         "speedup_vs_bf16_attention": round(attn_ms / fms, 3),
+                         "kernel": "attn_kernel Q8 (lf_block_sparse_attn_fp8)"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, host0, w.k_frames, w.k_blocks, args.cpu_sample_qblocks)

@@ -85,7 +85,12 @@ constexpr int WAVES_PER_SIMD = sizeof(T) == 2 && WPQ > 1 ? 2 : 1;
 
 // One workgroup's walk: per-wavefront query fragments and accumulators, the
 // scalar tile producer, the LDS loader and the per-tile math.
-template <typename T, int D, int WPQ, int QPWT = 4 / WPQ, bool SPLIT_PITCH = false>
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Q8 (bf16 walks only): queries and keys arrive as E4M3 codes with one E8M0
+// scale per 32 channels of a token; the scores are formed with the scaled
+// FP8 MFMA (32x32x64), everything after them as in the bf16 walk.
+template <typename T, int D, int WPQ, int QPWT = 4 / WPQ, bool SPLIT_PITCH = false, bool Q8 = false>
 struct Walk {
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -106,7 +111,11 @@ struct Walk {
   // keeps 32 bytes for both, since there the wider V rows' extra load
   // instruction and pad traffic cost more than the conflicts (measured).
   static constexpr bool kSplitPitch = SPLIT_PITCH && ES == 2 && D == 128;
-  static constexpr int RSK = D * ES + (kSplitPitch ? 16 : 32);  // K row pitch in bytes
+  static constexpr int KES = Q8 ? 1 : ES;                       // bytes per key element
+  static constexpr int CPRK = D * KES / 16;                     // 16-byte chunks per key row
+  // (FP8 key rows: 16-byte pad, the two 16-byte reads per lane of a row
+  // then fall in distinct bank groups)
+  static constexpr int RSK = D * KES + (Q8 ? 16 : (kSplitPitch ? 16 : 32));  // K row pitch in bytes
   static constexpr int RSV = D * ES + (kSplitPitch ? 64 : 32);  // V row pitch in bytes
   static constexpr int SPRK = RSK / 16, SPRV = RSV / 16;       // 16-byte slots per row (CPR data + pad)
   static constexpr int SLOTS_K = BN * SPRK, SLOTS_V = BN * SPRV;
@@ -114,6 +123,7 @@ struct Walk {
   static constexpr int LIV = (SLOTS_V + NT - 1) / NT;          // ... per V tile
   static constexpr int LI = LIK > LIV ? LIK : LIV;
   static constexpr int TILE_BYTES_K = BN * RSK, TILE_BYTES_V = BN * RSV;
+  static constexpr int TILE_ALLOC_K = TILE_BYTES_K + (Q8 ? 4 * BN : 0);  // Q8: + one scale word per key
   static constexpr int QSTEPS = D / M::KSTEP;
   static constexpr int DB = D / 32;
   static_assert(SLOTS_K % 64 == 0 && SLOTS_V % 64 == 0, "whole load instructions");
@@ -125,11 +135,15 @@ struct Walk {
   const KGeom& g;
   const T* kc;
   const T* vc;
+  const uint8_t* kc8;   // Q8: key codes [B,H,S,T,D]
+  const uint8_t* ksc8;  // Q8: key scales [B,H,S,T,D/32]
   int lane, wv, h, l32, lq, nrows, qr, qb0;
   bool wave_active;
   int64_t bh, qrow0;
   // per-wavefront state
-  frag qf[QSTEPS];
+  frag qf[Q8 ? 1 : QSTEPS];
+  i32x8 qf8[Q8 ? D / 64 : 1];  // Q8: this lane's query codes for each 64-channel step
+  uint32_t qsw;                // Q8: its four block scales, shifted so byte 2t serves step t
   f32x16 o[DB];
   float m_run, l_run, c2;
   // producer state (uniform)
@@ -169,17 +183,17 @@ struct Walk {
   // (lane l the l-th); this lane's slot holds chunk c of key row `row`, i.e.
   // byte offset row*D*ES + c*16 from the tile's first key.
   uint32_t doffk[LIK], doffv[LIV];
-  static __device__ __forceinline__ uint32_t slot_offset(int slot, int spr) {
+  static __device__ __forceinline__ uint32_t slot_offset(int slot, int spr, int cpr, int row_bytes) {
     const int row = min(slot / spr, BN - 1);
     int c = slot - (slot / spr) * spr;
-    while (c >= CPR) c -= CPR;  // a pad slot re-reads a chunk its row already loads (same cache line)
-    return (uint32_t)(row * D * ES + c * 16);
+    while (c >= cpr) c -= cpr;  // a pad slot re-reads a chunk its row already loads (same cache line)
+    return (uint32_t)(row * row_bytes + c * 16);
   }
   __device__ __forceinline__ void init_loads() {
 #pragma unroll
-    for (int i = 0; i < LIK; ++i) doffk[i] = slot_offset((i * NW + wv) * 64 + lane, SPRK);
+    for (int i = 0; i < LIK; ++i) doffk[i] = slot_offset((i * NW + wv) * 64 + lane, SPRK, CPRK, D * KES);
 #pragma unroll
-    for (int i = 0; i < LIV; ++i) doffv[i] = slot_offset((i * NW + wv) * 64 + lane, SPRV);
+    for (int i = 0; i < LIV; ++i) doffv[i] = slot_offset((i * NW + wv) * 64 + lane, SPRV, CPR, D * ES);
   }
 
   // The next tile's loads, described at the top of an iteration and issued
@@ -189,7 +203,7 @@ struct Walk {
   // zeros for rows past `count`, so a ragged tile needs no per-lane clamping
   // and no load leaves the tile.
   struct Next {
-    __amdgpu_buffer_rsrc_t rk, rv;
+    __amdgpu_buffer_rsrc_t rk, rv, rks;  // rks: Q8 key scales of the tile
     char* kd;
     char* vd;
   };
@@ -201,7 +215,14 @@ struct Walk {
   __device__ __forceinline__ Next next_tile(char* kd, char* vd, int64_t off, int count) const {
     Next n;
     const int bytes = count * D * ES;
-    n.rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(uniform_ptr(kc + off)), (short)0, bytes, kRawBufferFlags);
+    if constexpr (Q8) {  // key codes (one byte each) and their scales (D/32 bytes per key)
+      n.rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(uniform_ptr(kc8 + off)), (short)0, count * D,
+                                               kRawBufferFlags);
+      n.rks = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(uniform_ptr(ksc8 + off / 32)), (short)0,
+                                                count * (D / 32), kRawBufferFlags);
+    } else {
+      n.rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(uniform_ptr(kc + off)), (short)0, bytes, kRawBufferFlags);
+    }
     n.rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(uniform_ptr(vc + off)), (short)0, bytes, kRawBufferFlags);
     n.kd = kd;
     n.vd = vd;
@@ -220,9 +241,15 @@ struct Walk {
       if ((i + 1) * NT <= SLOTS || L0 < SLOTS)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(V ? n.rv : n.rk, LDS_PTR(void, (V ? n.vd : n.kd) + L0 * 16), 16,
                                                  V ? doffv[i] : doffk[i], 0, 0, 0);
+      if constexpr (Q8 && !V) {  // the 64 keys' scale words, 4 bytes per lane, behind the key tile
+        static_assert(D == 128, "one 4-byte scale word per key");
+        if (i == 0 && wv == 0)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(n.rks, LDS_PTR(void, n.kd + TILE_BYTES_K), 4, lane * 4, 0, 0, 0);
+      }
 #else
       (void)n;
       (void)L0;
+      (void)SLOTS;
 #endif
     }
   }
@@ -441,6 +468,47 @@ struct Walk {
 #undef LF_FENCE
   }
 
+  // ---- FP8 scores (Q8) ----------------------------------------------------
+  // Fragment of key half kh for the 64-channel step t of the scaled FP8 MFMA
+  // (32x32x64): lane half h holds channels 64t+16h .. +15 in bytes 0..15 and
+  // 64t+32+16h .. +15 in bytes 16..31. With this split the MFMA's two scale
+  // blocks per step are the contiguous channels 64t .. 64t+31 (its scale
+  // from lane half 0) and 64t+32 .. 64t+63 (lane half 1), i.e. the tensors'
+  // own 32-channel MX blocks. Queries are loaded the same way.
+  __device__ __forceinline__ i32x8 load_k8(const char* ks, int kh, int t) const {
+    const char* row = ks + (kh * 32 + l32) * RSK + 64 * t + 16 * h;
+    const uint4 a = *reinterpret_cast<const uint4*>(row);
+    const uint4 b = *reinterpret_cast<const uint4*>(row + 32);
+    return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  }
+  // This lane's key's scale word, shifted so that byte 2t holds the scale of
+  // the block the lane half serves in step t (the MFMA picks byte 2t).
+  __device__ __forceinline__ uint32_t kscale_word(const char* ks, int kh) const {
+    return *reinterpret_cast<const uint32_t*>(ks + TILE_BYTES_K + (kh * 32 + l32) * 4) >> (8 * h);
+  }
+  template <int TT>
+  static __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c, uint32_t sa,
+                                                 uint32_t sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 2 * TT, (int)sa, 2 * TT, (int)sb);
+  }
+  static __device__ __forceinline__ f32x16 mfma8_step(int t, const i32x8& a, const i32x8& b, const f32x16& c,
+                                                      uint32_t sa, uint32_t sb) {
+    return t == 0 ? mfma8<0>(a, b, c, sa, sb) : mfma8<1>(a, b, c, sa, sb);  // (t is a constant after unrolling)
+  }
+  __device__ __forceinline__ float exact_half_q8(const char* ks, int kh, int count, f32x16& s) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+    const uint32_t sw = kscale_word(ks, kh);
+#pragma unroll
+    for (int t = 0; t < D / 64; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      s = mfma8_step(t, load_k8(ks, kh, t), qf8[t], s, sw, qsw);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (count < (kh + 1) * 32) mask_half(s, kh, count);
+    return exact_from_scores(s);
+  }
+
   // ---- single-stage tile (one K and one V buffer per workgroup) ----------
   // Phase 1 reads only the K tile: S0, then S1 with the softmax of S0
   // between its MFMAs; this tile's V DMA goes out meanwhile (the V buffer was
@@ -483,6 +551,58 @@ struct Walk {
     float ps0 = psum(b0, b1);
     if (__builtin_amdgcn_ballot_w64(!(ps0 <= kFastLimit)) != 0) {
       exact_half(ks, 0, count, s0);
+      to_bf16(s0, b0, b1);
+      ps0 = psum(b0, b1);
+    }
+    l_run += ps0;
+    if (count < BN) mask_half(s1, 1, count);
+#undef LF_FENCE
+  }
+  // Phase 1 of the FP8 walk: the same as ss_phase1 with the scores of each
+  // half from D/64 scaled FP8 MFMAs (the V tile's loads spread over them).
+  __device__ __forceinline__ void ss_phase1_q8(const char* ks, int count, const Next& nv, f32x16& s1, bf16x8& b0,
+                                               bf16x8& b1) {
+#define LF_FENCE __builtin_amdgcn_sched_barrier(0)
+    constexpr int T8 = D / 64;
+    i32x8 kf[T8];
+    f32x16 s0;
+    const uint32_t sw0 = kscale_word(ks, 0), sw1 = kscale_word(ks, 1);
+#pragma unroll
+    for (int t = 0; t < T8; ++t) kf[t] = load_k8(ks, 0, t);
+    LF_FENCE;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = 0.0f;
+    constexpr int PER = (LI + 2 * T8 - 1) / (2 * T8);  // V loads per MFMA
+#pragma unroll
+    for (int t = 0; t < T8; ++t) {
+      s0 = mfma8_step(t, kf[t], qf8[t], s0, sw0, qsw);
+      kf[t] = load_k8(ks, 1, t);
+#pragma unroll
+      for (int u = 0; u < PER; ++u) issue_one<true>(nv, t * PER + u);
+      LF_FENCE;
+    }
+    if (count < 32) mask_half(s0, 0, count);
+    LF_FENCE;
+    const float mc = m_run * c2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s1[r] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < T8; ++t) {
+      s1 = mfma8_step(t, kf[t], qf8[t], s1, sw1, qsw);
+#pragma unroll
+      for (int u = 0; u < PER; ++u) issue_one<true>(nv, (T8 + t) * PER + u);
+      LF_FENCE;
+#pragma unroll
+      for (int u = 0; u < 16 / T8; ++u) {
+        const int r = t * (16 / T8) + u;
+        s0[r] = pin(__builtin_amdgcn_exp2f(fmaf(s0[r], c2, -mc)));
+      }
+      LF_FENCE;
+    }
+    to_bf16(s0, b0, b1);
+    float ps0 = psum(b0, b1);
+    if (__builtin_amdgcn_ballot_w64(!(ps0 <= kFastLimit)) != 0) {
+      exact_half_q8(ks, 0, count, s0);
       to_bf16(s0, b0, b1);
       ps0 = psum(b0, b1);
     }
@@ -600,19 +720,29 @@ struct Walk {
 // at b = 64, so four workgroups share a CU) and alternates them around two
 // barriers per tile: V of tile t streams in while tile t's scores are formed,
 // K of tile t+1 while its PV products run.
-template <typename T, int D, int WPQ, bool SS>
+// Q8 (single-stage bf16 walk, D = 128): q and k_cache are not read; the
+// scores come from the MX-FP8 codes and scales in f8.
+struct Fp8Operands {
+  const uint8_t* q;   // [B,H,Lq,D] E4M3 codes
+  const uint8_t* qs;  // [B,H,Lq,D/32] E8M0 scales
+  const uint8_t* k;   // [B,H,S,T,D]
+  const uint8_t* ks;  // [B,H,S,T,D/32]
+};
+
+template <typename T, int D, int WPQ, bool SS, bool Q8 = false>
 __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T, WPQ>)) void attn_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ nsel, int max_sel, float scale, const KGeom g, T* __restrict__ out,
-    float* __restrict__ lse) {
-  using W = Walk<T, D, WPQ, SS ? 1 : 4 / WPQ, !SS>;
+    float* __restrict__ lse, const Fp8Operands f8) {
+  static_assert(!Q8 || (SS && D == 128 && sizeof(T) == 2), "FP8 scores: single-stage bf16 walk, D = 128");
+  using W = Walk<T, D, WPQ, SS ? 1 : 4 / WPQ, !SS, Q8>;
   constexpr int QPW = W::QPW, ES = W::ES, QSTEPS = W::QSTEPS, DB = W::DB;
 
   // Two named stage buffers (not one indexed array): the loop below is
   // unrolled by two so every LDS read names its buffer at compile time, which
   // lets the compiler see that reading one stage never waits on the DMA that
   // is filling the other.
-  __shared__ __attribute__((aligned(1024))) char k0[W::TILE_BYTES_K];
+  __shared__ __attribute__((aligned(1024))) char k0[W::TILE_ALLOC_K];
   __shared__ __attribute__((aligned(1024))) char v0[W::TILE_BYTES_V];
   // History tiles of the walk, one entry each (see below); a block of more
   // than BN keys is two tiles.
@@ -645,7 +775,20 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
   w.qr = rg * 32 + w.l32;
   w.wave_active = rg * 32 < w.nrows;
   w.qrow0 = (int64_t)fc * g.T + (int64_t)jq * g.b;
-  {
+  if constexpr (Q8) {
+    w.kc8 = f8.k;
+    w.ksc8 = f8.ks;
+    const bool ok = w.qr < w.nrows;
+    const int64_t row = w.bh * g.Lq + w.qrow0 + (ok ? w.qr : 0);
+    const uint8_t* qp = f8.q + row * D;
+#pragma unroll
+    for (int t = 0; t < D / 64; ++t) {
+      const uint4 a = ok ? *reinterpret_cast<const uint4*>(qp + 64 * t + 16 * w.h) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 b = ok ? *reinterpret_cast<const uint4*>(qp + 64 * t + 32 + 16 * w.h) : make_uint4(0u, 0u, 0u, 0u);
+      w.qf8[t] = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    }
+    w.qsw = (ok ? *reinterpret_cast<const uint32_t*>(f8.qs + row * (D / 32)) : 0u) >> (8 * w.h);
+  } else {
     const bool ok = w.qr < w.nrows;
     const T* qp = q + (w.bh * g.Lq + w.qrow0 + (ok ? w.qr : 0)) * D;
 #pragma unroll
@@ -784,7 +927,10 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
       const typename W::Next nv = w.next_tile(k0, v0, c_off, c_cnt);
       f32x16 s1;
       bf16x8 b0, b1;
-      w.ss_phase1(k0, c_cnt, nv, s1, b0, b1);
+      if constexpr (Q8)
+        w.ss_phase1_q8(k0, c_cnt, nv, s1, b0, b1);
+      else
+        w.ss_phase1(k0, c_cnt, nv, s1, b0, b1);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this tile's V has landed (own share)
       __syncthreads();                       // ... everyone's, and nobody reads K any more
       int64_t n_off = c_off;
@@ -869,7 +1015,7 @@ hipError_t launch_typed(const KGeom& g, const void* q, const void* k, const void
   const unsigned grid = (unsigned)((int64_t)g.B * g.H * ((g.nqb + QPW - 1) / QPW));
   hipLaunchKernelGGL((attn_kernel<T, D, WPQ, SS>), dim3(grid), dim3(64 * WPQ * QPW), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sel, nsel, max_sel,
-                     scale, g, static_cast<T*>(out), lse);
+                     scale, g, static_cast<T*>(out), lse, Fp8Operands{});
   return hipGetLastError();
 }
 
@@ -889,6 +1035,18 @@ hipError_t launch_d(const KGeom& g, const void* q, const void* k, const void* v,
 }
 
 }  // namespace
+
+hipError_t launch_attention_fp8(const KGeom& g, const uint8_t* q8, const uint8_t* q_scale, const uint8_t* k8_cache,
+                                const uint8_t* k_scale, const void* v_cache, const int32_t* sel_blocks,
+                                const int32_t* n_sel, int32_t max_sel, float scale, void* out, float* lse,
+                                hipStream_t stream) {
+  if (g.D != 128 || g.b <= 32 || g.b > 64) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((int64_t)g.B * g.H * g.nqb);
+  hipLaunchKernelGGL((attn_kernel<__bf16, 128, 2, true, true>), dim3(grid), dim3(128), 0, stream, nullptr, nullptr,
+                     static_cast<const __bf16*>(v_cache), sel_blocks, n_sel, max_sel, scale, g,
+                     static_cast<__bf16*>(out), lse, Fp8Operands{q8, q_scale, k8_cache, k_scale});
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const KGeom& g, int32_t dtype, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel, float scale, void* out,

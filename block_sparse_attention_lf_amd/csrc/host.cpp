@@ -230,6 +230,32 @@ lf_status lf_block_sparse_attn(const lf_geom* g, const void* q, const void* k_ca
                     "lf_block_sparse_attn launch");
 }
 
+lf_status lf_block_sparse_attn_fp8(const lf_geom* g, const uint8_t* q8, const uint8_t* q_scale, const uint8_t* k8_cache,
+                                   const uint8_t* k_scale, const void* v_cache, const int32_t* frame_slot,
+                                   const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel,
+                                   float softmax_scale, void* out, float* lse, lf_stream stream) {
+  if (frame_slot == nullptr) return fail(LF_ERR_NULL, "frame_slot is NULL");
+  lf::KGeom kg;
+  lf_status st = make_geom(g, frame_slot, &kg);
+  if (st != LF_OK) return st;
+  if (g->dtype != LF_BF16) return fail(LF_ERR_DTYPE, "the FP8 variant takes bf16 values and writes bf16");
+  if (g->head_dim != 128 || g->block <= 32 || g->block > 64)
+    return fail(LF_ERR_GEOM, "the FP8 variant needs head_dim 128 and 32 < block <= 64");
+  if (q8 == nullptr || q_scale == nullptr || k8_cache == nullptr || k_scale == nullptr || v_cache == nullptr ||
+      out == nullptr)
+    return fail(LF_ERR_NULL, "q8 / q_scale / k8_cache / k_scale / v_cache / out is NULL");
+  if (max_sel < 0 || max_sel > LF_MAX_SEL) return fail(LF_ERR_K, "max_sel must be in [0, LF_MAX_SEL]");
+  if (max_sel > 0 && (sel_blocks == nullptr || n_sel == nullptr))
+    return fail(LF_ERR_NULL, "sel_blocks / n_sel is NULL");
+  if (!aligned16(q8) || !aligned16(k8_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(q_scale) & 3u) != 0 || (reinterpret_cast<uintptr_t>(k_scale) & 3u) != 0)
+    return fail(LF_ERR_ALIGN, "codes / v_cache / out must be 16-byte aligned, scales 4-byte aligned");
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return fail(LF_ERR_ARG, "softmax_scale must be > 0");
+  return hip_status(lf::launch_attention_fp8(kg, q8, q_scale, k8_cache, k_scale, v_cache, sel_blocks, n_sel, max_sel,
+                                             softmax_scale, out, lse, static_cast<hipStream_t>(stream)),
+                    "lf_block_sparse_attn_fp8 launch");
+}
+
 lf_status lf_block_sparse_attn_bwd(const lf_geom* g, const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* frame_slot, const int32_t* sel_blocks, const int32_t* n_sel,
                                    int32_t max_sel, float softmax_scale, const void* out, const float* lse,

@@ -38,6 +38,12 @@ hipError_t launch_select_blocks(const KGeom& g, const float* q_blk, const float*
 hipError_t launch_attention(const KGeom& g, int32_t dtype, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel, float scale,
                             void* out, float* lse, hipStream_t stream);
+// launch_attention with MX-FP8 queries and keys (E4M3 codes, one E8M0 scale
+// per 32 channels) and bf16 values/output; D = 128, 32 < block <= 64.
+hipError_t launch_attention_fp8(const KGeom& g, const uint8_t* q8, const uint8_t* q_scale, const uint8_t* k8_cache,
+                                const uint8_t* k_scale, const void* v_cache, const int32_t* sel_blocks,
+                                const int32_t* n_sel, int32_t max_sel, float scale, void* out, float* lse,
+                                hipStream_t stream);
 // Backward of launch_attention (bf16): dq [B,H,Lq,D], dk/dv rows of the
 // frames in g.slot, delta [B,H,Lq] scratch; all float32.
 hipError_t launch_attention_bwd(const KGeom& g, const void* q, const void* k_cache, const void* v_cache,

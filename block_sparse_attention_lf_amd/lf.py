@@ -30,7 +30,7 @@ STATUS = {0: "LF_OK", -1: "LF_ERR_NULL", -2: "LF_ERR_GEOM", -3: "LF_ERR_DTYPE", 
 
 # Every symbol include/lf.h declares.
 EXPORTS = ("lf_compress", "lf_max_sel", "lf_select", "lf_max_sel_1d", "lf_select_blocks", "lf_pool_keys", "lf_select_fused", "lf_block_sparse_attn",
-           "lf_block_sparse_attn_bwd", "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error")
+           "lf_block_sparse_attn_fp8", "lf_block_sparse_attn_bwd", "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error")
 
 
 class LfError(RuntimeError):
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         "lf_select_blocks": (ctypes.c_int, [G, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P]),
         "lf_block_sparse_attn": (ctypes.c_int, [G, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32, ctypes.c_float,
                                                 _P, _P, _P]),
+        "lf_block_sparse_attn_fp8": (ctypes.c_int, [G, _P, _P, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32,
+                                                    ctypes.c_float, _P, _P, _P]),
         "lf_block_sparse_attn_bwd": (ctypes.c_int, [G, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32, ctypes.c_float,
                                                     _P, _P, _P, _P, _P, _P, _P, _P]),
         "lf_chunk_budget": (ctypes.c_int, [ctypes.c_int32, _F64P, _F64P, ctypes.POINTER(ctypes.c_uint8),
@@ -247,6 +249,30 @@ def lf_block_sparse_attn(g: lf_geom, q, k_cache, v_cache, frame_slot, sel_blocks
     _check(lib().lf_block_sparse_attn(ctypes.byref(g), _ptr(q), _ptr(k_cache), _ptr(v_cache), sp, _ptr(sel_blocks),
                                       _ptr(n_sel), max_sel, float(softmax_scale), _ptr(out), _ptr(lse),
                                       _stream(stream)), "lf_block_sparse_attn")
+
+
+def lf_block_sparse_attn_fp8(g: lf_geom, q8, q_scale, k8_cache, k_scale, v_cache, frame_slot, sel_blocks, n_sel,
+                             softmax_scale: float, out, lse=None, stream=None) -> None:
+    """lf_block_sparse_attn on MX-FP8 queries and keys (E4M3 codes + E8M0 scales per 32 channels; see include/lf.h)."""
+    D = g.head_dim
+    _need(q8, (g.batch, g.heads, g.q_len, D), torch.uint8, "q8")
+    _need(q_scale, (g.batch, g.heads, g.q_len, D // 32), torch.uint8, "q_scale")
+    kshape = (g.batch, g.heads, g.cache_slots, g.tokens_per_frame)
+    _need(k8_cache, kshape + (D,), torch.uint8, "k8_cache")
+    _need(k_scale, kshape + (D // 32,), torch.uint8, "k_scale")
+    _need(v_cache, kshape + (D,), torch.bfloat16, "v_cache")
+    _need(out, (g.batch, g.heads, g.q_len, D), torch.bfloat16, "out")
+    if lse is not None:
+        _need(lse, (g.batch, g.heads, g.q_len), torch.float32, "lse")
+    max_sel = 0 if sel_blocks is None else sel_blocks.shape[-1]
+    if sel_blocks is not None:
+        _need(sel_blocks, (g.batch, g.heads, g.n_qblocks, max_sel), torch.int32, "sel_blocks")
+        _need(n_sel, (g.batch, g.heads, g.n_qblocks), torch.int32, "n_sel")
+    arr, sp = _slots(frame_slot)
+    _check(lib().lf_block_sparse_attn_fp8(ctypes.byref(g), _ptr(q8), _ptr(q_scale), _ptr(k8_cache), _ptr(k_scale),
+                                          _ptr(v_cache), sp, _ptr(sel_blocks), _ptr(n_sel), max_sel,
+                                          float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "lf_block_sparse_attn_fp8")
 
 
 def lf_block_sparse_attn_bwd(g: lf_geom, q, k_cache, v_cache, frame_slot, sel_blocks, n_sel, softmax_scale: float,

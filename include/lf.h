@@ -9,8 +9,9 @@
  *              2.1 chunk-aware growth (CAG), 2.2 hierarchical sparse attention
  *              (HSA: token compression, two-stage mask selection, execution).
  *   [LF-press] press summary of the same paper, section 3 (hierarchical
- *              sparse attention), section 2 (chunk-aware growth) and
- *              section 4 (experiments, ablation paragraph).
+ *              sparse attention), section 2 (chunk-aware growth),
+ *              section 4 (experiments, ablation paragraph) and section 5
+ *              (deployment: FP8 with per-token activation scales).
  *   [SF]       Self Forcing news page, rolling KV cache paragraph.
  *   [RF]       Rolling Forcing page, section 3, dual cache / attention anchor.
  *
@@ -188,6 +189,29 @@ lf_status lf_select_blocks(const lf_geom* g, const float* q_blk, const float* k_
 lf_status lf_block_sparse_attn(const lf_geom* g, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* frame_slot, const int32_t* sel_blocks, const int32_t* n_sel,
                                int32_t max_sel, float softmax_scale, void* out, float* lse, lf_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * lf_block_sparse_attn with FP8 queries and keys ([LF-press] 5: the
+ * deployment runs in FP8 with per-token scales for activations; here that
+ * form is applied to the attention's score product). Same masks, outputs and
+ * validation as lf_block_sparse_attn; q and k_cache are replaced by
+ *   q8        [B, H, Lq, D]              uint8  OCP E4M3 codes (no infinities,
+ *                                               0x7F/0xFF are NaN)
+ *   q_scale   [B, H, Lq, D/32]           uint8  OCP MX E8M0 scales (2^(e-127),
+ *                                               0xFF NaN), one per 32 channels
+ *   k8_cache  [B, H, cache_slots, T, D]  uint8  E4M3 codes
+ *   k_scale   [B, H, cache_slots, T, D/32] uint8 E8M0 scales
+ * so channel c of a token stands for decode(code[c]) * 2^(scale[c/32]-127).
+ * v_cache and out are bf16 (g->dtype must be LF_BF16, else LF_ERR_DTYPE);
+ * head_dim must be 128 and 32 < block <= 64 (else LF_ERR_GEOM). The score
+ * products run on the scaled FP8 MFMA with float32 accumulation; P and V
+ * enter the PV product in bf16 as in lf_block_sparse_attn. Codes and v_cache
+ * and out must be 16-byte aligned, scales 4-byte aligned (LF_ERR_ALIGN).
+ * ------------------------------------------------------------------------- */
+lf_status lf_block_sparse_attn_fp8(const lf_geom* g, const uint8_t* q8, const uint8_t* q_scale,
+                                   const uint8_t* k8_cache, const uint8_t* k_scale, const void* v_cache,
+                                   const int32_t* frame_slot, const int32_t* sel_blocks, const int32_t* n_sel,
+                                   int32_t max_sel, float softmax_scale, void* out, float* lse, lf_stream stream);
 
 /* ---------------------------------------------------------------------------
  * Backward of lf_block_sparse_attn, for sparse fine-tuning ([LF-press] 4,

@@ -200,3 +200,28 @@ def test_backward_validation():
     g32 = lf.geom_of(w)
     g32.dtype = 0  # float32 inputs: the backward takes bf16 only
     assert call(g32) == -3
+
+
+def test_fp8_validation():
+    """The FP8 variant's argument checks (all decided before any device work)."""
+    w = I.WAN480P_CHUNK
+    L = lf.lib()
+    p = ctypes.c_void_p(4096)
+    sp = I.rotated_slots(w).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def call(g, scale=1.0, k8=p, ks=p, max_sel=30):
+        return L.lf_block_sparse_attn_fp8(ctypes.byref(g), p, p, k8, ks, p, sp, p, p, max_sel, ctypes.c_float(scale),
+                                          p, p, None)
+
+    g = lf.geom_of(w)
+    assert call(g, scale=0.0) == -8
+    assert call(g, k8=None) == -1
+    assert call(g, max_sel=lf.LF_MAX_SEL + 1) == -4
+    assert call(g, ks=ctypes.c_void_p(4098)) == -5  # scales must be 4-byte aligned
+    g32 = lf.geom_of(w)
+    g32.dtype = 0
+    assert call(g32) == -3
+    for field, value in (("head_dim", 64), ("block", 32), ("block", 65)):
+        gg = lf.geom_of(w)
+        setattr(gg, field, value)
+        assert call(gg) == -2, (field, value)
