@@ -4,24 +4,29 @@
 // current chunk, softmax(scale q k^T) v, with an fp32 online softmax.
 //
 // gfx950 design
-//   * A workgroup owns 128 query rows: QPW consecutive query blocks of one
-//     (batch, head), WPQ = ceil(block/32) wavefronts per query block, 32 rows
-//     per wavefront (QPW = 4/WPQ). All its wavefronts share every key tile of
-//     the current chunk. For the history they walk the merged, ascending
-//     union of their query blocks' selected blocks: a tile is loaded once and
-//     only the wavefronts whose query block selected it compute on it, so no
-//     MFMA work is spent on unselected keys.
+//   * WPQ = ceil(block/32) wavefronts per query block, 32 query rows each.
+//     Two walks share the tile math:
+//       - single-stage (bf16, 32 < block <= 64): a workgroup is one query
+//         block; LDS holds one K and one V tile (four workgroups per CU).
+//         Per tile, the V tile streams in under the score MFMAs and the
+//         next K tile under the PV MFMAs, with a barrier between the phases.
+//       - double-buffered (every other case): a workgroup owns 128 query
+//         rows (4/WPQ query blocks of one head) and walks the ascending,
+//         de-duplicated union of their selected history blocks; a tile is
+//         loaded once and only the wavefronts whose query block selected it
+//         compute on it. One barrier per tile.
+//     Either walk starts with the current chunk's tiles, then the history
+//     tiles of a table built in LDS at the start of the workgroup.
 //   * Work is dealt XCD-aware: the hardware hands workgroups round-robin to
 //     the 8 XCDs, so workgroup w is remapped such that each XCD gets one
 //     contiguous range of (batch, head, query-block group) items; query
 //     blocks of one head then share that head's keys/values in one L2.
-//   * Key/value tiles of BN=64 keys stream HBM -> LDS with global_load_lds
-//     (16 bytes per lane, no registers), double-buffered: tile t+1 is in
-//     flight while tile t is computed, one barrier per tile. Rows are stored
-//     row-major with the 16-byte chunks of row r XOR-swizzled by r, so the
-//     MFMA operand reads below are spread over the LDS banks. Rows past the
-//     end of a ragged tile load a copy of the last valid row (finite data,
-//     masked to -inf / weight 0), so no lane reads outside the cache.
+//   * Key/value tiles of BN = 64 keys go HBM -> LDS with buffer loads that
+//     write LDS directly (16 bytes per lane, no registers). Each tile's
+//     buffer resource covers only its valid rows, so rows past the end of a
+//     ragged block read as zeros (then masked) and no load leaves the tile.
+//     LDS rows are padded so the fragment reads spread over the banks and
+//     every fragment address is one per-lane base plus a constant.
 //   * MFMA 32x32x16 bf16 (32x32x2 f32 for fp32 inputs). Scores are formed
 //     transposed, S^T = K Q^T (A = K from LDS, B = this wavefront's 32
 //     queries, kept in registers for the whole walk), so each lane holds one
@@ -30,8 +35,16 @@
 //     from registers. The A operand V^T comes from the row-major V tile with
 //     ds_read_tr16_b64: inside each 16-lane group it hands lane i element
 //     i&3 of source lane 4e+(i>>2), i.e. four consecutive keys of one column.
-//   * exp2 with the scale folded into log2(e) units; rows past the end of a
-//     ragged query block are computed on zero queries and never stored.
+//   * Online softmax in fp32 with exp2 (scale folded into log2(e) units)
+//     against the running maximum, without a per-tile maximum; a rarely
+//     taken exact branch rescales when a half's probabilities could grow too
+//     large. The normaliser sums the same bf16 P the PV product uses.
+//   * FP8 variant (press summary section 5: FP8 with per-token activation
+//     scales; single-stage walk, D = 128): queries and keys as E4M3 codes
+//     with E8M0 scales per 32 channels of a token, scores on the scaled FP8
+//     MFMA (32x32x64); V, P and the rest as in the bf16 walk.
+//   * Rows past the end of a ragged query block are computed on zero
+//     queries and never stored.
 #include "mfma.h"
 
 namespace lf {
@@ -759,9 +772,7 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
   w.l32 = w.lane & 31;
 
   // XCD-aware remap of the workgroup id to a work item (bh, query-block group).
-  const int nwg = gridDim.x, wg = blockIdx.x;
-  const int xcd = wg & 7, idx = wg >> 3, per = nwg >> 3, rem = nwg & 7;
-  const int item = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
   const int groups = (g.nqb + QPW - 1) / QPW;
   w.bh = item / groups;
   w.qb0 = (item - (int)w.bh * groups) * QPW;

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(64 * WPQ) void bwd_dq_kernel(const __bf16* __restri
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t item = blockIdx.x;  // (b*H + h)*nqb + qb
+  const int64_t item = xcd_item(blockIdx.x, gridDim.x);  // (b*H + h)*nqb + qb
   const int64_t bh = item / g.nqb;
   const int qb = (int)(item - bh * g.nqb);
   const int fc = qb / g.nb, jq = qb - fc * g.nb;
@@ -370,8 +370,9 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void bwd_dkv_kernel(con
   const int hpb = g.b > 64 ? 2 : 1;
   const int gpf = (g.T + KEYS - 1) / KEYS;  // key groups per current frame
   const int per_bh = CUR ? g.Fc * gpf : g.Fh * g.nb * hpb;
-  const int64_t bh = blockIdx.x / per_bh;
-  const int ti = (int)(blockIdx.x - bh * per_bh);
+  const int wgi = xcd_item(blockIdx.x, gridDim.x);
+  const int64_t bh = wgi / per_bh;
+  const int ti = (int)(wgi - bh * per_bh);
   int f, start, count, hist_id = -1;
   if constexpr (CUR) {
     const int f2 = ti / gpf;

@@ -35,4 +35,14 @@ __device__ inline P* uniform_ptr(P* p) {
   return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
 }
 
+// XCD-aware work order. The hardware deals consecutive workgroup ids
+// round-robin to the 8 XCDs (each with its own L2); this maps workgroup id
+// wg of nwg to a work item such that each XCD gets one contiguous range of
+// items, so neighbouring items (the query blocks of one head, which read
+// the same keys and values) share one L2.
+__device__ inline int xcd_item(int wg, int nwg) {
+  const int xcd = wg & 7, idx = wg >> 3, per = nwg >> 3, rem = nwg & 7;
+  return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
 }  // namespace lf
