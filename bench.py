@@ -52,6 +52,8 @@ def parse():
                     help="also time lf_block_sparse_attn_bwd (bf16) and report it under 'backward'")
     ap.add_argument("--fp8", action="store_true",
                     help="also time lf_block_sparse_attn_fp8 (MX-FP8 q/k) on the same selections; report under 'fp8'")
+    ap.add_argument("--rollout", action="store_true",
+                    help="also run the 7-chunk x 4-step rollout (chunk-aware budget per chunk); report under 'rollout'")
     ap.add_argument("--cpu-sample-qblocks", type=int, default=0, help="0: every query block (the whole call)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one elementwise kernel that reads and writes this many MiB "
@@ -100,6 +102,61 @@ def traffic_from_profiles(kernel_src: str, workload: str):
     if rec.get("kernel_source_sha256_16") != file_hash(kernel_src) or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def rollout(warmup: int):
+    """The chunk-wise rollout: chunk i (3 frames) attends to every earlier chunk, 4 denoise steps per chunk
+    with fresh queries, keys/values drawn once per chunk; chunk 0 runs dense, chunks 1-6 take the chunk-aware
+    budget. Each call (compress + select + attention, plus the host slot table) is timed with HIP events;
+    the whole cache (21 frames) is resident. Returns per-chunk and total figures."""
+    import torch
+
+    from block_sparse_attention_lf_amd import inputs as I
+    from block_sparse_attention_lf_amd import lf
+
+    r = I.CHUNK_ROLLOUT
+    n = r.n_chunks
+    hist = [r.chunk_frames * i for i in range(n)]
+    bud = lf.lf_chunk_budget(r.sigmas(), None, [True] + [False] * (n - 1), r.s_base, r.s_target, hist, None,
+                             r.blocks_per_frame, r.k_frames_min)
+    full = I.rollout_chunk_inputs(r, n - 1, 0)  # the cache with every chunk's keys/values
+    kc = torch.from_numpy(full["k_cache"]).to(torch.bfloat16).cuda()
+    vc = torch.from_numpy(full["v_cache"]).to(torch.bfloat16).cuda()
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / math.sqrt(r.head_dim)
+    chunks = []
+    tot_ms, tot_flops = 0.0, 0.0
+    for i in range(n):
+        kf, kb = bud["k_frames"][i], bud["k_blocks"][i]
+        w = r.chunk_workload(i, kf, kb)
+        g = lf.geom_of(w)
+        bufs = lf.Buffers(g, kf, kb)
+        slots = np.arange(w.hist_frames + w.chunk_frames, dtype=np.int32)
+        qs = [torch.from_numpy(I.rollout_chunk_inputs(r, i, st, kv_prev=full)["q"]).to(torch.bfloat16).cuda()
+              for st in range(r.steps)]
+        for j in range(warmup):
+            lf.hsa_attention(g, qs[j % r.steps], kc, vc, slots, bufs, scale, stream)
+        torch.cuda.synchronize()
+        ms, fl = [], []
+        for st in range(r.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            lf.hsa_attention(g, qs[st], kc, vc, slots, bufs, scale, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+            fl.append(effective_flops(w, bufs.sel_blocks.cpu().numpy(), bufs.n_sel.cpu().numpy()))
+        sel_blocks = int(bufs.n_sel[0, 0, 0].item())
+        chunks.append({"chunk": i, "hist_frames": w.hist_frames, "k_frames": kf, "k_blocks": kb,
+                       "sparsity": round(float(bud["sparsity"][i]), 4), "blocks_selected_per_qblock": sel_blocks,
+                       "ms_per_call": round(float(np.mean(ms)), 4), "effective_gflop_per_call": round(np.mean(fl) / 1e9, 2),
+                       "tflops": round(float(np.sum(fl)) / (float(np.sum(ms)) * 1e-3) / 1e12, 1)})
+        tot_ms += float(np.sum(ms))
+        tot_flops += float(np.sum(fl))
+    return {"name": r.name, "calls": n * r.steps, "total_ms": round(tot_ms, 3),
+            "total_effective_gflop": round(tot_flops / 1e9, 1),
+            "tflops": round(tot_flops / (tot_ms * 1e-3) / 1e12, 1), "beta": round(float(bud["beta"]), 6),
+            "chunks": chunks}
 
 
 def cpu_baseline(w, x, k_frames, k_blocks, sample_qblocks: int):
@@ -396,6 +453,9 @@ def main():
                          "frac_of_bf16_peak": round(fach / PEAK_BF16_TFLOPS, 4),
                          "speedup_vs_bf16_attention": round(attn_ms / fms, 3),
                          "kernel": "attn_kernel Q8 (lf_block_sparse_attn_fp8)"}
+    if args.rollout:
+        print("[bench] chunk rollout", file=sys.stderr, flush=True)
+        result["rollout"] = rollout(max(args.warmup, 1))
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, host0, w.k_frames, w.k_blocks, args.cpu_sample_qblocks)
