@@ -100,3 +100,8 @@ def test_backward_empty_history():
 def test_backward_wan480p_shape_two_heads():
     """The 480p chunk's shapes (T=1560, b=64, Fc=3, Fh=6, 80%) on unit-normal inputs; heads 0-1 checked."""
     _run(I.WAN480P_CHUNK.replace(dist="normal", seed=11), heads_checked=[0, 1])
+
+
+def test_backward_selection_lists_near_lf_max_sel():
+    """508 selected history blocks per query block (254 frames, 2 of 4 blocks each)."""
+    _run(_odd(128, 256, 64, Fc=1, Fh=254, H=1, kf=254, kb=2, n_sink=0, slots=255).replace(chunk_index=300))

@@ -122,3 +122,9 @@ def test_fp8_wan480p_chunk_sampled():
 def test_fp8_long_history_sink_sampled():
     w = I.LONG_HISTORY_SINK
     _run(w, qblocks=P.sample_qblocks(w, n_random=2))
+
+
+def test_fp8_selection_lists_near_lf_max_sel():
+    """508 selected history blocks per query block (254 frames, 2 of 4 blocks each)."""
+    w = _odd(256, 64, Fc=1, Fh=254, H=1, kf=254, kb=2, n_sink=0, slots=255).replace(chunk_index=300)
+    _run(w)

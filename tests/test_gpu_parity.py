@@ -187,3 +187,14 @@ def test_many_frames_and_blocks_limits():
                     chunk_frames=1, hist_frames=2, n_sink=0, cache_slots=3, dtype="bf16", k_frames=1, k_blocks=70,
                     sparsity=float("nan"), seed=9, dist="normal", chunk_index=2)
     _full_check(w2, n_random=3)
+
+
+@pytest.mark.parametrize("d,T,b,Fh,kb", [(64, 128, 16, 128, 4), (128, 256, 64, 254, 2)])
+def test_selection_lists_at_lf_max_sel(d, T, b, Fh, kb):
+    """Every query block selects LF_MAX_SEL (512) or 508 history blocks (every frame, half of its blocks):
+    the longest walks the kernels take, in the double-buffered (b = 16) and single-stage (b = 64) walks."""
+    w = I.Workload(name=f"maxsel_d{d}_b{b}", batch=1, heads=1, head_dim=d, grid=(1, T), block=b, chunk_frames=1,
+                   hist_frames=Fh, n_sink=0, cache_slots=Fh + 1, dtype="bf16", k_frames=Fh, k_blocks=kb,
+                   sparsity=float("nan"), seed=12, dist="normal", chunk_index=Fh)
+    assert lf.lf_max_sel(lf.geom_of(w), Fh, kb) in (lf.LF_MAX_SEL, lf.LF_MAX_SEL - 4)
+    _full_check(w, all_rows=True)
