@@ -363,6 +363,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void bwd_dkv_kernel(con
   __shared__ __attribute__((aligned(1024))) char gs1[MAXQ * S::RS];
   __shared__ float ls0[MAXQ], ls1[MAXQ], ds0[MAXQ], ds1[MAXQ];
   __shared__ int qlist[QCAP];
+  __shared__ uint32_t qmask[QCAP / 32];
   __shared__ int qcount;
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
@@ -417,21 +418,40 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void bwd_dkv_kernel(con
 
   for (int c0 = 0; c0 < g.nqb; c0 += QCAP) {
     // The query blocks in [c0, c0 + QCAP) that see this tile, ascending.
+    const int nqc = min(QCAP, g.nqb - c0);
     __syncthreads();  // the previous batch's list is consumed
+    if (hist_id >= 0) {
+      // A history tile is seen by the query blocks whose lists name its
+      // block. The batch's rows of sel are one contiguous array: every
+      // thread scans a strided share of it with U loads in flight at a time
+      // and marks a query block's bit in qmask where its block id appears
+      // at a position below the block's list length (staged in qlist).
+      for (int i = tid; i < QCAP / 32; i += NT) qmask[i] = 0u;
+      for (int i = tid; i < nqc; i += NT) qlist[i] = max_sel > 0 ? min(max(nsel[bh * g.nqb + c0 + i], 0), max_sel) : 0;
+      __syncthreads();
+      const int32_t* rows = sel + (bh * g.nqb + c0) * (int64_t)max_sel;
+      const int n_ent = nqc * max_sel;
+      constexpr int U = 8;
+      for (int e0 = tid; e0 < n_ent; e0 += NT * U) {
+        int x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = e0 + u * NT < n_ent ? rows[e0 + u * NT] : -1;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (x[u] == hist_id) {
+            const int e = e0 + u * NT, qi = e / max_sel;
+            if (e - qi * max_sel < qlist[qi]) atomicOr(&qmask[qi >> 5], 1u << (qi & 31));
+          }
+      }
+      __syncthreads();
+    }
     if (wv == 0) {
       int n = 0;
-      for (int k0 = c0; k0 < min(c0 + QCAP, g.nqb); k0 += 64) {
-        const int qb = k0 + lane;
-        bool sees = qb < min(c0 + QCAP, g.nqb);
-        if (sees && hist_id >= 0) {
-          const int64_t item = bh * g.nqb + qb;
-          const int len = max_sel > 0 ? min(max(nsel[item], 0), max_sel) : 0;
-          bool found = false;
-          for (int e = 0; e < len; ++e) found = found || sel[item * max_sel + e] == hist_id;
-          sees = found;
-        }
+      for (int k0 = 0; k0 < nqc; k0 += 64) {
+        const int qi = k0 + lane;
+        const bool sees = qi < nqc && (hist_id < 0 || ((qmask[qi >> 5] >> (qi & 31)) & 1u) != 0);
         const uint64_t m = __builtin_amdgcn_ballot_w64(sees);
-        if (sees) qlist[n + __builtin_popcountll(m & ((1ull << lane) - 1ull))] = qb;
+        if (sees) qlist[n + __builtin_popcountll(m & ((1ull << lane) - 1ull))] = c0 + qi;
         n += __builtin_popcountll(m);
       }
       if (lane == 0) qcount = n;
