@@ -415,7 +415,7 @@ def main():
                               "achieved": round(bflops / (bms * 1e-3) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
                               "frac": round(bflops / (bms * 1e-3) / 1e12 / peak, 4),
                               "kernels": "bwd_dq_kernel + bwd_dkv_kernel (dV pass, dK pass)"}
-    if args.fp8 and w.dtype == "bf16" and w.head_dim == 128 and 32 < w.block <= 64:
+    if args.fp8 and w.dtype == "bf16" and w.head_dim == 128:
         # The same attention calls with queries and keys as MX-FP8 (E4M3 codes,
         # one E8M0 scale per 32 channels, quantised on the host, untimed) and
         # the bf16 step's selections. Score products run at the FP8 MFMA rate

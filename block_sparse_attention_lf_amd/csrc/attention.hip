@@ -670,8 +670,97 @@ struct Walk {
 #undef LF_FENCE
   }
 
+  // One tile of the double-buffered walk with FP8 scores: compute_bf16 with
+  // each half's scores from D/64 scaled FP8 MFMAs; the next tile's K loads
+  // ride along the first half's, its V loads along the second half's.
+  __device__ __forceinline__ void compute_q8(const char* ks, const char* vs, int count, const Next& nx) {
+#define LF_FENCE __builtin_amdgcn_sched_barrier(0)
+    constexpr int T8 = D / 64;
+    constexpr int PK = (LIK + T8 - 1) / T8, PV = (LIV + T8 - 1) / T8;  // loads per MFMA
+    i32x8 kf[T8];
+    bf16x8 va[DB];
+    f32x16 s0, s1;
+    const uint32_t sw0 = kscale_word(ks, 0), sw1 = kscale_word(ks, 1);
+#pragma unroll
+    for (int t = 0; t < T8; ++t) kf[t] = load_k8(ks, 0, t);
+    LF_FENCE;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < T8; ++t) {
+      s0 = mfma8_step(t, kf[t], qf8[t], s0, sw0, qsw);
+      kf[t] = load_k8(ks, 1, t);
+#pragma unroll
+      for (int u = 0; u < PK; ++u) issue_one<false>(nx, t * PK + u);
+      LF_FENCE;
+    }
+    if (count < 32) mask_half(s0, 0, count);
+    LF_FENCE;
+    float mc = m_run * c2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s1[r] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < T8; ++t) {
+      s1 = mfma8_step(t, kf[t], qf8[t], s1, sw1, qsw);
+      LF_FENCE;
+#pragma unroll
+      for (int u = 0; u < 16 / T8; ++u) {
+        const int r = t * (16 / T8) + u;
+        s0[r] = pin(__builtin_amdgcn_exp2f(fmaf(s0[r], c2, -mc)));
+      }
+#pragma unroll
+      for (int u = 0; u < PV; ++u) issue_one<true>(nx, t * PV + u);
+      LF_FENCE;
+    }
+    load_v(vs, 0, va);
+    bf16x8 b0, b1;
+    to_bf16(s0, b0, b1);
+    float ps0 = psum(b0, b1);
+    if (__builtin_amdgcn_ballot_w64(!(ps0 <= kFastLimit)) != 0) {
+      exact_half_q8(ks, 0, count, s0);
+      to_bf16(s0, b0, b1);
+      ps0 = psum(b0, b1);
+    }
+    l_run += ps0;
+    if (count < BN) mask_half(s1, 1, count);
+    LF_FENCE;
+    mc = m_run * c2;
+#pragma unroll
+    for (int j = 0; j < 2 * DB; ++j) {
+      const int ps = j / DB, db = j % DB;
+      o[db] = M::mfma(va[db], ps == 0 ? b0 : b1, o[db]);
+      va[db] = load_v1(vs, ps + 1, db);
+      LF_FENCE;
+#pragma unroll
+      for (int u = 0; u < 16 / (2 * DB); ++u) {
+        const int r = j * (16 / (2 * DB)) + u;
+        s1[r] = pin(__builtin_amdgcn_exp2f(fmaf(s1[r], c2, -mc)));
+      }
+      LF_FENCE;
+    }
+    to_bf16(s1, b0, b1);
+    float ps1 = psum(b0, b1);
+    if (__builtin_amdgcn_ballot_w64(!(ps1 <= kFastLimit)) != 0) {
+      exact_half_q8(ks, 1, count, s1);
+      to_bf16(s1, b0, b1);
+      ps1 = psum(b0, b1);
+    }
+    l_run += ps1;
+    LF_FENCE;
+#pragma unroll
+    for (int j = 0; j < 2 * DB; ++j) {
+      const int ps = 2 + j / DB, db = j % DB;
+      o[db] = M::mfma(va[db], ps == 2 ? b0 : b1, o[db]);
+      if (ps == 2) va[db] = load_v1(vs, 3, db);
+      LF_FENCE;
+    }
+#undef LF_FENCE
+  }
+
   __device__ __forceinline__ void compute(const char* ks, const char* vs, int count, const Next& nx) {
-    if constexpr (ES == 2) {
+    if constexpr (Q8) {
+      compute_q8(ks, vs, count, nx);
+    } else if constexpr (ES == 2) {
       compute_bf16(ks, vs, count, nx);
     } else {
       issue(nx);
@@ -733,8 +822,8 @@ struct Walk {
 // at b = 64, so four workgroups share a CU) and alternates them around two
 // barriers per tile: V of tile t streams in while tile t's scores are formed,
 // K of tile t+1 while its PV products run.
-// Q8 (single-stage bf16 walk, D = 128): q and k_cache are not read; the
-// scores come from the MX-FP8 codes and scales in f8.
+// Q8 (bf16 values, D = 128): q and k_cache are not read; the scores come
+// from the MX-FP8 codes and scales in f8.
 struct Fp8Operands {
   const uint8_t* q;   // [B,H,Lq,D] E4M3 codes
   const uint8_t* qs;  // [B,H,Lq,D/32] E8M0 scales
@@ -747,7 +836,7 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ nsel, int max_sel, float scale, const KGeom g, T* __restrict__ out,
     float* __restrict__ lse, const Fp8Operands f8) {
-  static_assert(!Q8 || (SS && D == 128 && sizeof(T) == 2), "FP8 scores: single-stage bf16 walk, D = 128");
+  static_assert(!Q8 || (D == 128 && sizeof(T) == 2), "FP8 scores: bf16 values, D = 128");
   using W = Walk<T, D, WPQ, SS ? 1 : 4 / WPQ, !SS, Q8>;
   constexpr int QPW = W::QPW, ES = W::ES, QSTEPS = W::QSTEPS, DB = W::DB;
 
@@ -957,7 +1046,7 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
       c_msk = n_msk;
     }
   } else {
-  __shared__ __attribute__((aligned(1024))) char k1[W::TILE_BYTES_K];
+  __shared__ __attribute__((aligned(1024))) char k1[W::TILE_ALLOC_K];
   __shared__ __attribute__((aligned(1024))) char v1[W::TILE_BYTES_V];
   // Double-buffered walk, unrolled by two so each half names its buffers.
   // A wavefront computes a tile only if its query block selected it; with a
@@ -1030,6 +1119,17 @@ hipError_t launch_typed(const KGeom& g, const void* q, const void* k, const void
   return hipGetLastError();
 }
 
+template <int WPQ, bool SS>
+hipError_t launch_fp8_typed(const KGeom& g, const Fp8Operands& f8, const void* v, const int32_t* sel,
+                            const int32_t* nsel, int max_sel, float scale, void* out, float* lse, hipStream_t stream) {
+  constexpr int QPW = SS ? 1 : 4 / WPQ;
+  const unsigned grid = (unsigned)((int64_t)g.B * g.H * ((g.nqb + QPW - 1) / QPW));
+  hipLaunchKernelGGL((attn_kernel<__bf16, 128, WPQ, SS, true>), dim3(grid), dim3(64 * WPQ * QPW), 0, stream, nullptr,
+                     nullptr, static_cast<const __bf16*>(v), sel, nsel, max_sel, scale, g, static_cast<__bf16*>(out),
+                     lse, f8);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_d(const KGeom& g, const void* q, const void* k, const void* v, const int32_t* sel,
                     const int32_t* nsel, int max_sel, float scale, void* out, float* lse, hipStream_t stream) {
@@ -1051,12 +1151,14 @@ hipError_t launch_attention_fp8(const KGeom& g, const uint8_t* q8, const uint8_t
                                 const uint8_t* k_scale, const void* v_cache, const int32_t* sel_blocks,
                                 const int32_t* n_sel, int32_t max_sel, float scale, void* out, float* lse,
                                 hipStream_t stream) {
-  if (g.D != 128 || g.b <= 32 || g.b > 64) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)((int64_t)g.B * g.H * g.nqb);
-  hipLaunchKernelGGL((attn_kernel<__bf16, 128, 2, true, true>), dim3(grid), dim3(128), 0, stream, nullptr, nullptr,
-                     static_cast<const __bf16*>(v_cache), sel_blocks, n_sel, max_sel, scale, g,
-                     static_cast<__bf16*>(out), lse, Fp8Operands{q8, q_scale, k8_cache, k_scale});
-  return hipGetLastError();
+  if (g.D != 128) return hipErrorInvalidValue;
+  const Fp8Operands f8{q8, q_scale, k8_cache, k_scale};
+  switch ((g.b + 31) / 32) {
+    case 1: return launch_fp8_typed<1, false>(g, f8, v_cache, sel_blocks, n_sel, max_sel, scale, out, lse, stream);
+    case 2: return launch_fp8_typed<2, true>(g, f8, v_cache, sel_blocks, n_sel, max_sel, scale, out, lse, stream);
+    case 3: return launch_fp8_typed<3, false>(g, f8, v_cache, sel_blocks, n_sel, max_sel, scale, out, lse, stream);
+    default: return launch_fp8_typed<4, false>(g, f8, v_cache, sel_blocks, n_sel, max_sel, scale, out, lse, stream);
+  }
 }
 
 hipError_t launch_attention(const KGeom& g, int32_t dtype, const void* q, const void* k_cache, const void* v_cache,

@@ -239,8 +239,7 @@ lf_status lf_block_sparse_attn_fp8(const lf_geom* g, const uint8_t* q8, const ui
   lf_status st = make_geom(g, frame_slot, &kg);
   if (st != LF_OK) return st;
   if (g->dtype != LF_BF16) return fail(LF_ERR_DTYPE, "the FP8 variant takes bf16 values and writes bf16");
-  if (g->head_dim != 128 || g->block <= 32 || g->block > 64)
-    return fail(LF_ERR_GEOM, "the FP8 variant needs head_dim 128 and 32 < block <= 64");
+  if (g->head_dim != 128) return fail(LF_ERR_GEOM, "the FP8 variant needs head_dim 128");
   if (q8 == nullptr || q_scale == nullptr || k8_cache == nullptr || k_scale == nullptr || v_cache == nullptr ||
       out == nullptr)
     return fail(LF_ERR_NULL, "q8 / q_scale / k8_cache / k_scale / v_cache / out is NULL");

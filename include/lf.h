@@ -203,7 +203,7 @@ lf_status lf_block_sparse_attn(const lf_geom* g, const void* q, const void* k_ca
  *   k_scale   [B, H, cache_slots, T, D/32] uint8 E8M0 scales
  * so channel c of a token stands for decode(code[c]) * 2^(scale[c/32]-127).
  * v_cache and out are bf16 (g->dtype must be LF_BF16, else LF_ERR_DTYPE);
- * head_dim must be 128 and 32 < block <= 64 (else LF_ERR_GEOM). The score
+ * head_dim must be 128 (else LF_ERR_GEOM). The score
  * products run on the scaled FP8 MFMA with float32 accumulation; P and V
  * enter the PV product in bf16 as in lf_block_sparse_attn. Codes and v_cache
  * and out must be 16-byte aligned, scales 4-byte aligned (LF_ERR_ALIGN).

@@ -93,9 +93,11 @@ def _odd(T, b, Fc=2, Fh=4, H=2, kf=2, kb=2, n_sink=1, slots=None, dist="normal")
                       k_blocks=kb, sparsity=float("nan"), seed=9, dist=dist, chunk_index=4)
 
 
-@pytest.mark.parametrize("T,b", [(200, 64), (130, 64), (100, 48), (77, 40), (64, 64), (33, 33)])
+@pytest.mark.parametrize("T,b", [(200, 64), (130, 64), (100, 48), (77, 40), (64, 64), (33, 33), (77, 16), (100, 32),
+                                 (200, 96), (300, 128), (128, 128), (130, 65)])
 def test_fp8_odd_geometries(T, b):
-    """Ragged last blocks, blocks shorter than a 64-key tile, one-block frames."""
+    """Ragged last blocks, blocks shorter than a 64-key tile, one-block frames; blocks of up to 32 keys (four
+    query blocks per workgroup) and of 65-128 keys (two 64-key tiles per block) take the double-buffered walk."""
     _run(_odd(T, b))
 
 
@@ -117,6 +119,12 @@ def test_fp8_wan480p_chunk_sampled():
     """The 480p chunk at full size (12 heads, 4680 queries, 6 history frames), sampled query blocks."""
     w = I.WAN480P_CHUNK
     _run(w, qblocks=P.sample_qblocks(w))
+
+
+def test_fp8_wide_head_sampled():
+    """40 heads, 3600-token frames, 128-token blocks (double-buffered walk), sampled query blocks."""
+    w = I.WIDE_HEAD
+    _run(w, qblocks=P.sample_qblocks(w, n_random=2))
 
 
 def test_fp8_long_history_sink_sampled():

@@ -221,7 +221,7 @@ def test_fp8_validation():
     g32 = lf.geom_of(w)
     g32.dtype = 0
     assert call(g32) == -3
-    for field, value in (("head_dim", 64), ("block", 32), ("block", 65)):
+    for field, value in (("head_dim", 64), ("block", 129)):
         gg = lf.geom_of(w)
         setattr(gg, field, value)
         assert call(gg) == -2, (field, value)
