@@ -121,8 +121,10 @@ __device__ inline void store_acc_t(float* dst, const f32x16& acc, int db, int h,
 }
 
 // Tile t of a query block's walk, from index t on: the current chunk's
-// 64-key tiles, then the tiles of its selected history blocks (ignored ids
-// skipped). On return t is the tile found; false when the walk is over.
+// KT-key tiles, then the tiles of its selected history blocks (ignored ids
+// skipped; a block is hpb = ceil(b / KT) tiles). On return t is the tile
+// found; false when the walk is over.
+template <int KT>
 __device__ inline bool dq_tile(const KGeom& g, const int32_t* sel, int64_t item, int max_sel, int tpf, int n_cur,
                                int hpb, int64_t bh, int& t, int n_tiles, int64_t& base, int& count) {
   for (; t < n_tiles; ++t) {
@@ -130,16 +132,16 @@ __device__ inline bool dq_tile(const KGeom& g, const int32_t* sel, int64_t item,
     if (t < n_cur) {
       const int f2 = t / tpf, tt = t - f2 * tpf;
       slot = g.slot[g.Fh + f2];
-      start = tt * 64;
-      count = min(64, g.T - start);
+      start = tt * KT;
+      count = min(KT, g.T - start);
     } else {
       const int e = (t - n_cur) / hpb, half = (t - n_cur) - e * hpb;
       const int x = sel[item * max_sel + e];
       if (x < 0 || x >= g.Fh * g.nb) continue;  // ignored id
       const int f = x / g.nb, jb = x - f * g.nb;
       slot = g.slot[f];
-      start = jb * g.b + half * 64;
-      count = min(64, min(jb * g.b + g.b, g.T) - start);
+      start = jb * g.b + half * KT;
+      count = min(KT, min(jb * g.b + g.b, g.T) - start);
       if (count <= 0) continue;
     }
     base = ((bh * g.S + slot) * (int64_t)g.T + start) * g.D;
@@ -148,14 +150,14 @@ __device__ inline bool dq_tile(const KGeom& g, const int32_t* sel, int64_t item,
   return false;
 }
 
-// One tile of the dQ walk on the stage (ks, vs), `count` valid keys.
-template <int D>
+// One tile of the dQ walk on the stage (ks, vs): KT keys, `count` valid.
+template <int D, int KT>
 __device__ inline void dq_tile_math(const char* ks, const char* vs, int count, const bf16x8* qf, const bf16x8* dof,
                                     f32x16* acc, float c2, float lse2, float dd, int lane) {
   using S = BwdShape<D>;
   const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
+  for (int kh = 0; kh < KT / 32; ++kh) {
     f32x16 s, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -184,9 +186,12 @@ __device__ inline void dq_tile_math(const char* ks, const char* vs, int count, c
 }
 
 // ---------------------------------------------------------------------------
-// dQ (and D_i): one workgroup of WPQ wavefronts per (batch, head, query block).
-template <int D, int WPQ>
-__global__ __launch_bounds__(64 * WPQ) void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
+// dQ (and D_i): one workgroup of WPQ wavefronts per (batch, head, query
+// block), walking key tiles of KT keys. With KT = 32 the four stage buffers
+// take 37 KB of LDS (D = 128), so workgroups share a CU two wavefronts per
+// SIMD (registers capped at 256 to match).
+template <int D, int WPQ, int KT>
+__global__ __launch_bounds__(64 * WPQ, (KT == 32 ? 2 : 1)) void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                                                           const __bf16* __restrict__ vc, const __bf16* __restrict__ out,
                                                           const __bf16* __restrict__ dout, const float* __restrict__ lse,
                                                           const int32_t* __restrict__ sel,
@@ -197,10 +202,10 @@ __global__ __launch_bounds__(64 * WPQ) void bwd_dq_kernel(const __bf16* __restri
   constexpr int NT = 64 * WPQ;
   // Double-buffered K/V stages, separate arrays so the compiler sees that the
   // fragment reads of one stage never wait on the loads filling the other.
-  __shared__ __attribute__((aligned(1024))) char ks0[64 * S::RS];
-  __shared__ __attribute__((aligned(1024))) char vs0[64 * S::RS];
-  __shared__ __attribute__((aligned(1024))) char ks1[64 * S::RS];
-  __shared__ __attribute__((aligned(1024))) char vs1[64 * S::RS];
+  __shared__ __attribute__((aligned(1024))) char ks0[KT * S::RS];
+  __shared__ __attribute__((aligned(1024))) char vs0[KT * S::RS];
+  __shared__ __attribute__((aligned(1024))) char ks1[KT * S::RS];
+  __shared__ __attribute__((aligned(1024))) char vs1[KT * S::RS];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -239,16 +244,16 @@ __global__ __launch_bounds__(64 * WPQ) void bwd_dq_kernel(const __bf16* __restri
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-  const int tpf = (g.T + 63) / 64;
+  const int tpf = (g.T + KT - 1) / KT;
   const int n_cur = g.Fc * tpf;
-  const int hpb = g.b > 64 ? 2 : 1;
+  const int hpb = (g.b + KT - 1) / KT;
   const int len = max_sel > 0 ? min(max(nsel[item], 0), max_sel) : 0;
   const int n_tiles = n_cur + len * hpb;
-  TileDma<D, 64, NT> dma;
+  TileDma<D, KT, NT> dma;
   dma.init(tid);
   int t = 0, count = 0, ncount = 0;
   int64_t nbase = 0;
-  bool have = dq_tile(g, sel, item, max_sel, tpf, n_cur, hpb, bh, t, n_tiles, nbase, ncount);
+  bool have = dq_tile<KT>(g, sel, item, max_sel, tpf, n_cur, hpb, bh, t, n_tiles, nbase, ncount);
   if (have) {
     dma.issue(ks0, kc + nbase, ncount, tid);
     dma.issue(vs0, vc + nbase, ncount, tid);
@@ -260,14 +265,14 @@ __global__ __launch_bounds__(64 * WPQ) void bwd_dq_kernel(const __bf16* __restri
   {                                                                                      \
     count = ncount;                                                                      \
     ++t;                                                                                 \
-    const bool more = dq_tile(g, sel, item, max_sel, tpf, n_cur, hpb, bh, t, n_tiles, nbase, ncount); \
+    const bool more = dq_tile<KT>(g, sel, item, max_sel, tpf, n_cur, hpb, bh, t, n_tiles, nbase, ncount); \
     __builtin_amdgcn_s_waitcnt(kWaitVm0);                                                \
     __syncthreads();                                                                     \
     if (more) {                                                                          \
       dma.issue(KB, kc + nbase, ncount, tid);                                            \
       dma.issue(VB, vc + nbase, ncount, tid);                                            \
     }                                                                                    \
-    dq_tile_math<D>(KA, VA, count, qf, dof, acc, c2, lse2, dd, lane);                    \
+    dq_tile_math<D, KT>(KA, VA, count, qf, dof, acc, c2, lse2, dd, lane);                \
     have = more;                                                                         \
   }
   while (have) {
@@ -524,6 +529,10 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void bwd_dkv_kernel(con
   }
 }
 
+// Key tile width of the dQ walk (32: two wavefronts per SIMD; 64: one, with
+// half the tiles).
+constexpr int kDqKeys = 32;
+
 template <int D>
 hipError_t launch_bwd_d(const KGeom& g, const void* q, const void* k, const void* v, const int32_t* sel,
                         const int32_t* nsel, int max_sel, float scale, const void* out, const float* lse,
@@ -536,19 +545,19 @@ hipError_t launch_bwd_d(const KGeom& g, const void* q, const void* k, const void
   const unsigned nq = (unsigned)((int64_t)g.B * g.H * g.nqb);
   switch ((g.b + 31) / 32) {
     case 1:
-      hipLaunchKernelGGL((bwd_dq_kernel<D, 1>), dim3(nq), dim3(64), 0, stream, Q, K, V, O, G, lse, sel, nsel, max_sel,
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 1, kDqKeys>), dim3(nq), dim3(64), 0, stream, Q, K, V, O, G, lse, sel, nsel, max_sel,
                          scale, g, delta, dq);
       break;
     case 2:
-      hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), dim3(nq), dim3(128), 0, stream, Q, K, V, O, G, lse, sel, nsel,
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 2, kDqKeys>), dim3(nq), dim3(128), 0, stream, Q, K, V, O, G, lse, sel, nsel,
                          max_sel, scale, g, delta, dq);
       break;
     case 3:
-      hipLaunchKernelGGL((bwd_dq_kernel<D, 3>), dim3(nq), dim3(192), 0, stream, Q, K, V, O, G, lse, sel, nsel,
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 3, kDqKeys>), dim3(nq), dim3(192), 0, stream, Q, K, V, O, G, lse, sel, nsel,
                          max_sel, scale, g, delta, dq);
       break;
     default:
-      hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), dim3(nq), dim3(256), 0, stream, Q, K, V, O, G, lse, sel, nsel,
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 4, kDqKeys>), dim3(nq), dim3(256), 0, stream, Q, K, V, O, G, lse, sel, nsel,
                          max_sel, scale, g, delta, dq);
       break;
   }
