@@ -350,7 +350,7 @@ __device__ inline void dkv_block_math(const char* qs, const char* gs, const floa
 // head). Tiles per (batch, head): the current chunk's Fc * ceil(T/64) tiles,
 // then every history block's tile(s) (blocks of more than 64 keys are two).
 template <int D, int MAXQ, int MODE, int NW, bool CUR>
-__global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void bwd_dkv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
+__global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_dkv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                                                       const __bf16* __restrict__ vc, const __bf16* __restrict__ dout,
                                                       const float* __restrict__ lse, const float* __restrict__ delta,
                                                       const int32_t* __restrict__ sel,
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void bwd_dkv_kernel(con
   using S = BwdShape<D>;
   constexpr int NT = 64 * NW;
   constexpr int KEYS = 32 * NW;  // keys per workgroup
-  constexpr int QCAP = 1024;     // query blocks listed per batch
+  constexpr int QCAP = MAXQ <= 32 ? 512 : 1024;  // query blocks listed per batch
   __shared__ __attribute__((aligned(1024))) char qs0[MAXQ * S::RS];
   __shared__ __attribute__((aligned(1024))) char gs0[MAXQ * S::RS];
   __shared__ __attribute__((aligned(1024))) char qs1[MAXQ * S::RS];
@@ -464,33 +464,45 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void bwd_dkv_kernel(con
     __syncthreads();
     const int nq = qcount;
     if (nq == 0) continue;
-    // Stage the first query block; then per block: wait, barrier, start the
-    // next block's loads into the other stage, compute, and write the next
-    // block's lse / delta rows (loaded before its tiles, so already here).
-    int i = 0, nrows = 0;
-    int64_t row0 = 0;
-    {
-      const int qb = qlist[0];
+    // Steps of at most MAXQ query rows: a query block of more rows is taken
+    // in several steps. Stage the first step; then per step: wait, barrier,
+    // start the next step's loads into the other stage, compute, and write
+    // the next step's lse / delta rows (loaded before its tiles, so already
+    // here).
+    // Rows [r0, r0 + rows) of step (ii, hh): part hh of query block qlist[ii],
+    // which has qrows rows in all.
+    auto locate = [&](int ii, int hh, int64_t& r0, int& rows, int& qrows) {
+      const int qb = qlist[ii];
       const int fc = qb / g.nb, jq = qb - fc * g.nb;
-      nrows = min(g.b, g.T - jq * g.b);
-      row0 = bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b;
-      if (tid < MAXQ) {
-        ls0[tid] = tid < nrows ? lse[row0 + tid] * kLog2e : INFINITY;  // +inf: P = 0 on missing rows
-        if constexpr (DK) ds0[tid] = tid < nrows ? delta[row0 + tid] : 0.0f;
-      }
-      dma.issue(qs0, q + row0 * D, nrows, tid);
-      dma.issue(gs0, dout + row0 * D, nrows, tid);
+      qrows = min(g.b, g.T - jq * g.b);
+      r0 = bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b + (int64_t)hh * MAXQ;
+      rows = min(MAXQ, qrows - hh * MAXQ);
+    };
+    int i = 0, hq = 0, nrows = 0, qrows = 0;
+    int64_t row0 = 0;
+    locate(0, 0, row0, nrows, qrows);
+    if (tid < MAXQ) {
+      ls0[tid] = tid < nrows ? lse[row0 + tid] * kLog2e : INFINITY;  // +inf: P = 0 on missing rows
+      if constexpr (DK) ds0[tid] = tid < nrows ? delta[row0 + tid] : 0.0f;
     }
+    dma.issue(qs0, q + row0 * D, nrows, tid);
+    dma.issue(gs0, dout + row0 * D, nrows, tid);
+    bool have = true;
 #define LF_DKV_STEP(QA, GA, LA, DA, QB, GB, LB, DB_)                                          \
   {                                                                                         \
     const int cur_rows = nrows;                                                             \
-    const bool more = i + 1 < nq;                                                           \
+    bool more = true;                                                                       \
+    if ((hq + 1) * MAXQ < qrows) {                                                          \
+      ++hq;                                                                                 \
+    } else if (i + 1 < nq) {                                                                \
+      ++i;                                                                                  \
+      hq = 0;                                                                               \
+    } else {                                                                                \
+      more = false;                                                                         \
+    }                                                                                       \
     float nl = 0.0f, nd = 0.0f;                                                             \
     if (more) {                                                                             \
-      const int qb = qlist[i + 1];                                                          \
-      const int fc = qb / g.nb, jq = qb - fc * g.nb;                                        \
-      nrows = min(g.b, g.T - jq * g.b);                                                     \
-      row0 = bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b;                             \
+      locate(i, hq, row0, nrows, qrows);                                                    \
       if (tid < nrows) {                                                                    \
         nl = lse[row0 + tid];                                                               \
         if constexpr (DK) nd = delta[row0 + tid];                                           \
@@ -507,11 +519,11 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void bwd_dkv_kernel(con
       LB[tid] = tid < nrows ? nl * kLog2e : INFINITY;                                       \
       if constexpr (DK) DB_[tid] = nd;                                                      \
     }                                                                                       \
-    ++i;                                                                                    \
+    have = more;                                                                            \
   }
-    while (i < nq) {
+    while (have) {
       LF_DKV_STEP(qs0, gs0, ls0, ds0, qs1, gs1, ls1, ds1)
-      if (i >= nq) break;
+      if (!have) break;
       LF_DKV_STEP(qs1, gs1, ls1, ds1, qs0, gs0, ls0, ds0)
     }
 #undef LF_DKV_STEP
@@ -576,7 +588,7 @@ hipError_t launch_bwd_d(const KGeom& g, const void* q, const void* k, const void
   hipLaunchKernelGGL((bwd_dkv_kernel<D, MAXQ, 1, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta,  \
                      sel, nsel, max_sel, scale, g, dk, nullptr);                                                       \
   if (nhist > 0)                                                                                                       \
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, MAXQ, 2, 2, false>), dim3(nhist), dim3(128), 0, stream, Q, K, V, G, lse,    \
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 32, 2, 2, false>), dim3(nhist), dim3(128), 0, stream, Q, K, V, G, lse,      \
                        delta, sel, nsel, max_sel, scale, g, dv, dk);
   if (g.b <= 64) {
     LF_DKV(64)
