@@ -414,7 +414,7 @@ def main():
         result["backward"] = {"ms_per_call": round(bms, 4), "algorithmic_flops": bflops,
                               "achieved": round(bflops / (bms * 1e-3) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
                               "frac": round(bflops / (bms * 1e-3) / 1e12 / peak, 4),
-                              "kernels": "bwd_dq_kernel + bwd_dkv_kernel (dV pass, dK pass)"}
+                              "kernels": "bwd_dq_kernel + bwd_dkv_kernel (current-chunk and history dK+dV passes)"}
     if args.fp8 and w.dtype == "bf16" and w.head_dim == 128:
         # The same attention calls with queries and keys as MX-FP8 (E4M3 codes,
         # one E8M0 scale per 32 channels, quantised on the host, untimed) and

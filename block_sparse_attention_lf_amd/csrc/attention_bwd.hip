@@ -191,7 +191,7 @@ __device__ inline void dq_tile_math(const char* ks, const char* vs, int count, c
 // take 37 KB of LDS (D = 128), so workgroups share a CU two wavefronts per
 // SIMD (registers capped at 256 to match).
 template <int D, int WPQ, int KT>
-__global__ __launch_bounds__(64 * WPQ, (KT == 32 ? 2 : 1)) void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
+__global__ __launch_bounds__(64 * WPQ, (KT == 32 && WPQ >= 2 ? 2 : 1)) void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                                                           const __bf16* __restrict__ vc, const __bf16* __restrict__ out,
                                                           const __bf16* __restrict__ dout, const float* __restrict__ lse,
                                                           const int32_t* __restrict__ sel,
@@ -346,9 +346,11 @@ __device__ inline void dkv_block_math(const char* qs, const char* gs, const floa
 }
 
 // ---------------------------------------------------------------------------
-// dK (DK) or dV: one workgroup of two wavefronts per key tile of one (batch,
-// head). Tiles per (batch, head): the current chunk's Fc * ceil(T/64) tiles,
-// then every history block's tile(s) (blocks of more than 64 keys are two).
+// dV (MODE 0), dK (MODE 1) or both (MODE 2) of the keys of one workgroup,
+// NW wavefronts of 32 keys each, walking the query blocks that see them
+// MAXQ rows at a time. CUR: key groups of the current chunk (Fc *
+// ceil(T / (32 NW)) per (batch, head)); otherwise one 64-key tile of a
+// history block (blocks of more than 64 keys are two).
 template <int D, int MAXQ, int MODE, int NW, bool CUR>
 __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_dkv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                                                       const __bf16* __restrict__ vc, const __bf16* __restrict__ dout,
@@ -574,28 +576,18 @@ hipError_t launch_bwd_d(const KGeom& g, const void* q, const void* k, const void
       break;
   }
   // Current-chunk keys are seen by every query block of the head: 256 keys
-  // per workgroup (eight wavefronts) so each staged query block feeds four
-  // times the MFMA work. History blocks have their own query blocks: one
-  // 64-key tile per workgroup.
+  // per workgroup (eight wavefronts) so each staged query block feeds eight
+  // wavefronts' MFMA work. History blocks have their own query blocks: one
+  // 64-key tile per workgroup. Both take dK and dV in one pass (S and P are
+  // formed once for both) and stage the query blocks 32 rows at a time, so
+  // a workgroup's stages fit 40 KB of LDS and two wavefronts share a SIMD.
   const unsigned ncur = (unsigned)((int64_t)g.B * g.H * g.Fc * ((g.T + 255) / 256));
   const unsigned nhist = (unsigned)((int64_t)g.B * g.H * g.Fh * g.nb * (g.b > 64 ? 2 : 1));
-  // (History workgroups are held to one wavefront per SIMD by their LDS, so
-  // they take dK and dV in one pass; the current-chunk passes run two
-  // wavefronts per SIMD and keep dK and dV apart to fit 256 registers.)
-#define LF_DKV(MAXQ)                                                                                                   \
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, MAXQ, 0, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta,  \
-                     sel, nsel, max_sel, scale, g, dv, nullptr);                                                       \
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, MAXQ, 1, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta,  \
-                     sel, nsel, max_sel, scale, g, dk, nullptr);                                                       \
-  if (nhist > 0)                                                                                                       \
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 32, 2, 2, false>), dim3(nhist), dim3(128), 0, stream, Q, K, V, G, lse,      \
-                       delta, sel, nsel, max_sel, scale, g, dv, dk);
-  if (g.b <= 64) {
-    LF_DKV(64)
-  } else {
-    LF_DKV(128)
-  }
-#undef LF_DKV
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, 32, 2, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta, sel,
+                     nsel, max_sel, scale, g, dv, dk);
+  if (nhist > 0)
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 32, 2, 2, false>), dim3(nhist), dim3(128), 0, stream, Q, K, V, G, lse, delta,
+                       sel, nsel, max_sel, scale, g, dv, dk);
   return hipGetLastError();
 }
 
