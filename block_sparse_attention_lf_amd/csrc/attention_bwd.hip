@@ -579,11 +579,13 @@ hipError_t launch_bwd_d(const KGeom& g, const void* q, const void* k, const void
   // per workgroup (eight wavefronts) so each staged query block feeds eight
   // wavefronts' MFMA work. History blocks have their own query blocks: one
   // 64-key tile per workgroup. Both take dK and dV in one pass (S and P are
-  // formed once for both) and stage the query blocks 32 rows at a time, so
-  // a workgroup's stages fit 40 KB of LDS and two wavefronts share a SIMD.
+  // formed once for both), with two wavefronts per SIMD (256 registers).
+  // The eight-wavefront current workgroups fill a CU on their own and
+  // stage up to 64 query rows per step (78 KB of LDS); the two-wavefront
+  // history workgroups stage 32 rows per step (40 KB), so four share a CU.
   const unsigned ncur = (unsigned)((int64_t)g.B * g.H * g.Fc * ((g.T + 255) / 256));
   const unsigned nhist = (unsigned)((int64_t)g.B * g.H * g.Fh * g.nb * (g.b > 64 ? 2 : 1));
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, 32, 2, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta, sel,
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, 64, 2, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta, sel,
                      nsel, max_sel, scale, g, dv, dk);
   if (nhist > 0)
     hipLaunchKernelGGL((bwd_dkv_kernel<D, 32, 2, 2, false>), dim3(nhist), dim3(128), 0, stream, Q, K, V, G, lse, delta,
