@@ -292,9 +292,9 @@ __global__ __launch_bounds__(64 * WPQ, (KT == 32 && WPQ >= 2 ? 2 : 1)) void bwd_
 // per 32 query rows, S = Q K^T and P; dV^T += dO^T P, or dP = dO V^T,
 // dS = P (dP - D) and dK^T += Q^T dS. ls holds lse*log2(e) per row (+inf on
 // missing rows, so their P is 0), dd the row's D.
-template <int D, int MODE>  // MODE: 0 dV, 1 dK, 2 both (acc = dV, acc2 = dK)
+template <int D>  // adv: dV^T accumulators, adk: dK^T accumulators
 __device__ inline void dkv_block_math(const char* qs, const char* gs, const float* ls, const float* dd, int nrows,
-                                      const bf16x8* kf, const bf16x8* vf, f32x16* acc, f32x16* acc2, float c2,
+                                      const bf16x8* kf, const bf16x8* vf, f32x16* adv, f32x16* adk, float c2,
                                       bool kok, int lane) {
   using S = BwdShape<D>;
   const int l32 = lane & 31, h = lane >> 5;
@@ -310,7 +310,7 @@ __device__ inline void dkv_block_math(const char* qs, const char* gs, const floa
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       p[r] = kok ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -ls[32 * qh + acc_row(r, h)])) : 0.0f;
-    if constexpr (MODE != 1) {  // dV^T += dO^T P
+    {  // dV^T += dO^T P
       bf16x8 b0, b1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -318,12 +318,11 @@ __device__ inline void dkv_block_math(const char* qs, const char* gs, const floa
       }
 #pragma unroll
       for (int db = 0; db < S::DB; ++db) {
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh, db, lane), b0, acc[db], 0, 0, 0);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh + 1, db, lane), b1, acc[db], 0, 0, 0);
+        adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh, db, lane), b0, adv[db], 0, 0, 0);
+        adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh + 1, db, lane), b1, adv[db], 0, 0, 0);
       }
     }
-    if constexpr (MODE != 0) {  // dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
-      f32x16* ak = MODE == 2 ? acc2 : acc;
+    {  // dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
       f32x16 dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) dp[r] = 0.0f;
@@ -338,28 +337,26 @@ __device__ inline void dkv_block_math(const char* qs, const char* gs, const floa
       }
 #pragma unroll
       for (int db = 0; db < S::DB; ++db) {
-        ak[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qs, 2 * qh, db, lane), b0, ak[db], 0, 0, 0);
-        ak[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qs, 2 * qh + 1, db, lane), b1, ak[db], 0, 0, 0);
+        adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qs, 2 * qh, db, lane), b0, adk[db], 0, 0, 0);
+        adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qs, 2 * qh + 1, db, lane), b1, adk[db], 0, 0, 0);
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// dV (MODE 0), dK (MODE 1) or both (MODE 2) of the keys of one workgroup,
-// NW wavefronts of 32 keys each, walking the query blocks that see them
+// dV and dK of the keys of one workgroup, NW wavefronts of 32 keys each, walking the query blocks that see them
 // MAXQ rows at a time. CUR: key groups of the current chunk (Fc *
 // ceil(T / (32 NW)) per (batch, head)); otherwise one 64-key tile of a
 // history block (blocks of more than 64 keys are two).
-template <int D, int MAXQ, int MODE, int NW, bool CUR>
+template <int D, int MAXQ, int NW, bool CUR>
 __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_dkv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                                                       const __bf16* __restrict__ vc, const __bf16* __restrict__ dout,
                                                       const float* __restrict__ lse, const float* __restrict__ delta,
                                                       const int32_t* __restrict__ sel,
                                                       const int32_t* __restrict__ nsel, int max_sel, float scale,
-                                                      const KGeom g, float* __restrict__ dst,
-                                                      float* __restrict__ dst2) {
-  constexpr bool DK = MODE != 0;  // needs V^T and D
+                                                      const KGeom g, float* __restrict__ dv,
+                                                      float* __restrict__ dk) {
   using S = BwdShape<D>;
   constexpr int NT = 64 * NW;
   constexpr int KEYS = 32 * NW;  // keys per workgroup
@@ -407,19 +404,16 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
 #pragma unroll
   for (int t = 0; t < S::QSTEPS; ++t) {
     kf[t] = own_frag(kc + (krow0 + (kok ? key : 0)) * D, kok, t, h);
-    if constexpr (DK) vf[t] = own_frag(vc + (krow0 + (kok ? key : 0)) * D, kok, t, h);
+    vf[t] = own_frag(vc + (krow0 + (kok ? key : 0)) * D, kok, t, h);
   }
-  f32x16 acc[S::DB], acc2[MODE == 2 ? S::DB : 1];
+  f32x16 adv[S::DB], adk[S::DB];
 #pragma unroll
   for (int db = 0; db < S::DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-  if constexpr (MODE == 2) {
-#pragma unroll
-    for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc2[db][r] = 0.0f;
-  }
+    for (int r = 0; r < 16; ++r) {
+      adv[db][r] = 0.0f;
+      adk[db][r] = 0.0f;
+    }
   TileDma<D, MAXQ, NT> dma;
   dma.init(tid);
 
@@ -485,7 +479,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
     locate(0, 0, row0, nrows, qrows);
     if (tid < MAXQ) {
       ls0[tid] = tid < nrows ? lse[row0 + tid] * kLog2e : INFINITY;  // +inf: P = 0 on missing rows
-      if constexpr (DK) ds0[tid] = tid < nrows ? delta[row0 + tid] : 0.0f;
+      ds0[tid] = tid < nrows ? delta[row0 + tid] : 0.0f;
     }
     dma.issue(qs0, q + row0 * D, nrows, tid);
     dma.issue(gs0, dout + row0 * D, nrows, tid);
@@ -507,7 +501,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
       locate(i, hq, row0, nrows, qrows);                                                    \
       if (tid < nrows) {                                                                    \
         nl = lse[row0 + tid];                                                               \
-        if constexpr (DK) nd = delta[row0 + tid];                                           \
+        nd = delta[row0 + tid];                                           \
       }                                                                                     \
     }                                                                                       \
     __builtin_amdgcn_s_waitcnt(kWaitVm0);                                                   \
@@ -516,10 +510,10 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
       dma.issue(QB, q + row0 * D, nrows, tid);                                              \
       dma.issue(GB, dout + row0 * D, nrows, tid);                                           \
     }                                                                                       \
-    dkv_block_math<D, MODE>(QA, GA, LA, DA, cur_rows, kf, vf, acc, acc2, c2, kok, lane);    \
+    dkv_block_math<D>(QA, GA, LA, DA, cur_rows, kf, vf, adv, adk, c2, kok, lane);           \
     if (more && tid < MAXQ) {                                                               \
       LB[tid] = tid < nrows ? nl * kLog2e : INFINITY;                                       \
-      if constexpr (DK) DB_[tid] = nd;                                                      \
+      DB_[tid] = nd;                                                      \
     }                                                                                       \
     have = more;                                                                            \
   }
@@ -532,14 +526,12 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no load may still be writing LDS when the workgroup ends
   if (!kok) return;
-  // MODE 0: dst = dV; MODE 1: dst = dK; MODE 2: dst = dV, dst2 = dK.
-  float* row = dst + (krow0 + key) * D;
+  float* vrow = dv + (krow0 + key) * D;
+  float* krow = dk + (krow0 + key) * D;
 #pragma unroll
-  for (int db = 0; db < S::DB; ++db) store_acc_t(row, acc[db], db, h, MODE == 1 ? scale : 1.0f);
-  if constexpr (MODE == 2) {
-    float* row2 = dst2 + (krow0 + key) * D;
-#pragma unroll
-    for (int db = 0; db < S::DB; ++db) store_acc_t(row2, acc2[db], db, h, scale);
+  for (int db = 0; db < S::DB; ++db) {
+    store_acc_t(vrow, adv[db], db, h, 1.0f);
+    store_acc_t(krow, adk[db], db, h, scale);
   }
 }
 
@@ -585,10 +577,10 @@ hipError_t launch_bwd_d(const KGeom& g, const void* q, const void* k, const void
   // history workgroups stage 32 rows per step (40 KB), so four share a CU.
   const unsigned ncur = (unsigned)((int64_t)g.B * g.H * g.Fc * ((g.T + 255) / 256));
   const unsigned nhist = (unsigned)((int64_t)g.B * g.H * g.Fh * g.nb * (g.b > 64 ? 2 : 1));
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, 64, 2, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta, sel,
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, 64, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta, sel,
                      nsel, max_sel, scale, g, dv, dk);
   if (nhist > 0)
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 32, 2, 2, false>), dim3(nhist), dim3(128), 0, stream, Q, K, V, G, lse, delta,
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 32, 2, false>), dim3(nhist), dim3(128), 0, stream, Q, K, V, G, lse, delta,
                        sel, nsel, max_sel, scale, g, dv, dk);
   return hipGetLastError();
 }
