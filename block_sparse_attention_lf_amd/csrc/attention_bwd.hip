@@ -1,7 +1,8 @@
 // Backward of the block-sparse attention (gradients of sum(out * dout)
 // through the same block masks), for sparse fine-tuning: the ablation
-// passage of the Light Forcing technical summary fine-tunes the model with
-// the sparse attention in place. With S = scale q k^T over the keys a query
+// paragraph of the Light Forcing press summary (section 4) compares the
+// sparse attention with and without fine-tuning the model around it. With
+// S = scale q k^T over the keys a query
 // block sees, P = softmax(S), O = P v:
 //   dV = P^T dO,  dP = dO v^T,  D_i = dO_i . O_i,  dS = P * (dP - D),
 //   dq = scale dS k,  dk = scale dS^T q.
@@ -11,18 +12,17 @@
 // gfx950 design (bf16 inputs, float32 gradients, MFMA 32x32x16 bf16 with
 // float32 accumulation; P and dS are rounded to bf16 as MFMA operands):
 //   * bwd_dq_kernel: one workgroup per query block (one wavefront per 32
-//     rows), walking the same tiles as the forward (the current chunk's
-//     64-key tiles, then the blocks of its selection). Per 32-key half:
-//     S^T = K Q^T and dP^T = V dO^T (Q^T, dO^T in registers), dS^T, then
-//     dQ^T += K^T dS^T with K^T read from the row-major tile by the
-//     transposing LDS read. It also writes D_i = dO_i . O_i for the key pass.
-//   * bwd_dkv_kernel: one workgroup per key tile (one wavefront per 32
-//     keys), walking the query blocks that see the tile (all of them for a
-//     current-chunk tile; those whose selection holds the block for a history
-//     tile). Per 32 query rows: S = Q K^T (K^T in registers), P; the dV pass
-//     adds dO^T P, the dK pass dP = dO V^T, dS and Q^T dS. Splitting dK and
-//     dV into two passes keeps each under 256 registers (two wavefronts per
-//     SIMD) at the price of computing S twice.
+//     rows), walking the keys the forward walks (the current chunk, then
+//     the blocks of its selection) in 32-key tiles: S^T = K Q^T and
+//     dP^T = V dO^T (Q^T, dO^T in registers), dS^T, then dQ^T += K^T dS^T
+//     with K^T read from the row-major tile by the transposing LDS read. It
+//     also writes D_i = dO_i . O_i for the key passes.
+//   * bwd_dkv_kernel: one workgroup per key group (one wavefront per 32
+//     keys; 256 keys of the current chunk, or one 64-key history tile),
+//     walking the query blocks that see it (all of them for current-chunk
+//     keys; those whose selection holds the block for a history tile) a
+//     few query rows at a time. Per 32 query rows: S = Q K^T (K^T, V^T in
+//     registers), P; dV^T += dO^T P; dP = dO V^T, dS, dK^T += Q^T dS.
 //   Each key row's gradient is summed inside one workgroup: no atomics, and
 //   every gradient row of a frame named by the slot table is written once
 //   (zero where no query sees it). Rows of other slots are not written.
