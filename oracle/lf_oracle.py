@@ -341,8 +341,8 @@ def attention_grad(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, fram
                    sel_blocks: np.ndarray, n_sel: np.ndarray, dout: np.ndarray, tokens_per_frame: int, block: int,
                    chunk_frames: int, hist_frames: int, scale: float) -> Dict[str, np.ndarray]:
     """Backward of ``attention`` for the loss sum(out * dout) (the gradient a
-    sparse fine-tuning step needs; the ablation passage of the technical
-    summary fine-tunes with the sparse attention in place).
+    sparse fine-tuning step needs; the press summary's ablation paragraph,
+    section 4, compares the sparse attention with and without fine-tuning).
 
     Each query block contributes through its own mask; key and value
     gradients of one cache row add up over every query block that sees it.
