@@ -136,3 +136,47 @@ def test_fp8_selection_lists_near_lf_max_sel():
     """508 selected history blocks per query block (254 frames, 2 of 4 blocks each)."""
     w = _odd(256, 64, Fc=1, Fh=254, H=1, kf=254, kb=2, n_sink=0, slots=255).replace(chunk_index=300)
     _run(w)
+
+
+def _fp8_call(w, x, q8, qs, k8, ks, sel, nsel, scale):
+    g = lf.geom_of(w)
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (q8, qs, k8, ks)]
+    vc = P.to_dev(x["v_cache"], "bf16")
+    sb = torch.from_numpy(np.ascontiguousarray(sel, np.int32)).cuda()
+    ns = torch.from_numpy(np.ascontiguousarray(nsel, np.int32)).cuda()
+    out = torch.empty((w.batch, w.heads, w.q_len, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    lf.lf_block_sparse_attn_fp8(g, *dev, vc, x["frame_slot"], sb, ns, scale, out, None)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("T,b", [(100, 16), (200, 64), (300, 128)])
+def test_fp8_ignored_ids_and_unsorted_lists(T, b):
+    """Ids of -1 or out of range and entries past n_sel change nothing (bit for bit); lists in descending
+    order (no shared tiles in the union walk of b = 16) still match the oracle."""
+    w = _odd(T, b, Fh=5, kf=3, kb=2)
+    _say(f"[fp8] ignored/unsorted {w.name}")
+    x = I.make_inputs(w)
+    q8, qs, k8, ks = _quantised(x)
+    _, s = P.oracle_compress_select(w, x, w.k_frames, w.k_blocks)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    base = _fp8_call(w, x, q8, qs, k8, ks, s["sel_blocks"], s["n_sel"], scale)
+    m = s["sel_blocks"].shape[-1]
+    noisy = np.full(s["sel_blocks"].shape[:-1] + (m + 6,), 10 ** 6, np.int32)
+    noisy[..., 1:m + 1] = s["sel_blocks"]
+    noisy[..., 0] = -1
+    noisy[..., m + 1] = w.hist_frames * w.blocks_per_frame
+    got = _fp8_call(w, x, q8, qs, k8, ks, noisy, s["n_sel"] + 2, scale)
+    assert np.array_equal(got, base)
+    rev = s["sel_blocks"].copy()
+    for idx in np.ndindex(rev.shape[:-1]):
+        n = s["n_sel"][idx]
+        rev[idx][:n] = rev[idx][:n][::-1].copy()
+    got_rev = _fp8_call(w, x, q8, qs, k8, ks, rev, s["n_sel"], scale)
+    qbs = [(0, h, qb) for h in range(w.heads) for qb in range(w.n_qblocks)]
+    a = O.attention_fp8(q8, qs, k8, ks, x["v_cache"], x["frame_slot"], s["sel_blocks"], s["n_sel"],
+                        w.tokens_per_frame, w.block, w.chunk_frames, w.hist_frames, scale, qblocks=qbs)
+    err = np.abs(got_rev.astype(np.float64) - a["out"])
+    assert err.max() <= P.MAX_ABS and err.mean() <= P.MEAN_ABS, (err.max(), err.mean())
+    rel = float(np.linalg.norm(got_rev - a["out"]) / np.linalg.norm(a["out"]))
+    assert rel <= P.REL_L2, rel
