@@ -225,3 +225,12 @@ def test_fp8_validation():
         gg = lf.geom_of(w)
         setattr(gg, field, value)
         assert call(gg) == -2, (field, value)
+
+
+def test_binding_limits_match_the_header():
+    """The binding's LF_MAX_* copies equal the #defines of include/lf.h."""
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lf.h")).read()
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(LF_MAX_\w+)\s+(\d+)", text)}
+    assert defs, "no LF_MAX_ limits found"
+    for name, value in defs.items():
+        assert getattr(lf, name) == value, name
