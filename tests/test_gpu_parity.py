@@ -116,7 +116,9 @@ def test_planted_structure_is_recovered():
 
 
 @pytest.mark.parametrize("dtype,d,T,b", [("bf16", 64, 100, 48), ("f32", 128, 200, 64), ("bf16", 128, 130, 128),
-                                         ("f32", 64, 77, 16), ("bf16", 64, 40, 8)])
+                                         ("f32", 64, 77, 16), ("bf16", 64, 40, 8), ("bf16", 128, 200, 64),
+                                         ("bf16", 128, 90, 40), ("bf16", 128, 250, 96), ("bf16", 64, 300, 128),
+                                         ("bf16", 128, 70, 32)])
 def test_odd_geometries(dtype, d, T, b):
     w = I.Workload(name=f"odd_{dtype}_{d}_{T}_{b}", batch=2, heads=3, head_dim=d, grid=(1, T), block=b,
                    chunk_frames=2, hist_frames=5, n_sink=1, cache_slots=8, dtype=dtype, k_frames=2, k_blocks=2,
