@@ -46,6 +46,18 @@
  *     enqueued. A failing call returns a negative lf_status and enqueues
  *     nothing. LF_ERR_HIP reports a launch failure; lf_last_error() gives the
  *     detail string (per thread). There is no other global state.
+ *
+ * One attention call of one layer at one denoise step of a chunk:
+ *   lf_cache_frame_slots(policy, S, n_sink, Fc, chunk, &Fh, frame_slot, ids);
+ *   lf_chunk_budget(...)  -> k_frames, k_blocks of this chunk
+ *   lf_compress(g, q, k_cache, frame_slot, q_blk, k_blk, k_frm, stream);
+ *   lf_select(g, q_blk, k_blk, k_frm, k_frames, k_blocks, NULL, sel_blocks,
+ *             n_sel, lf_max_sel(g, k_frames, k_blocks), stream);
+ *   lf_block_sparse_attn(g, q, k_cache, v_cache, frame_slot, sel_blocks,
+ *                        n_sel, max_sel, 1/sqrt(D), out, lse, stream);
+ * With pooling on commit, lf_pool_keys runs once per committed frame and
+ * lf_select_fused replaces lf_compress + lf_select. Buffers (q_blk ...
+ * sel_blocks) can be reused across calls of the same geometry.
  */
 #ifndef LF_H_
 #define LF_H_
