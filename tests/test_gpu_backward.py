@@ -105,3 +105,28 @@ def test_backward_wan480p_shape_two_heads():
 def test_backward_selection_lists_near_lf_max_sel():
     """508 selected history blocks per query block (254 frames, 2 of 4 blocks each)."""
     _run(_odd(128, 256, 64, Fc=1, Fh=254, H=1, kf=254, kb=2, n_sink=0, slots=255).replace(chunk_index=300))
+
+
+def test_backward_is_deterministic():
+    """No atomics: two calls on the same inputs give the same bits (480p shape, two heads)."""
+    w = I.WAN480P_CHUNK.replace(heads=2, dist="normal", seed=13, name="wan480p_h2")
+    x = I.make_inputs(w)
+    g = lf.geom_of(w)
+    q, kc, vc = P.device_inputs(w, x)
+    bufs = lf.Buffers(g, w.k_frames, w.k_blocks, with_lse=True)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    lf.hsa_attention(g, q, kc, vc, x["frame_slot"], bufs, scale)
+    dout = torch.from_numpy(np.random.default_rng(3).standard_normal(q.shape).astype(np.float32)).to(
+        torch.bfloat16).cuda()
+    res = []
+    for _ in range(2):
+        delta = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        dk = torch.zeros(kc.shape, dtype=torch.float32, device="cuda")
+        dv = torch.zeros(kc.shape, dtype=torch.float32, device="cuda")
+        lf.lf_block_sparse_attn_bwd(g, q, kc, vc, x["frame_slot"], bufs.sel_blocks, bufs.n_sel, scale, bufs.out,
+                                    bufs.lse, dout, delta, dq, dk, dv)
+        torch.cuda.synchronize()
+        res.append((dq.cpu(), dk.cpu(), dv.cpu()))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a, b)
