@@ -54,6 +54,8 @@ def parse():
                     help="also time lf_block_sparse_attn_fp8 (MX-FP8 q/k) on the same selections; report under 'fp8'")
     ap.add_argument("--rollout", action="store_true",
                     help="also run the 7-chunk x 4-step rollout (chunk-aware budget per chunk); report under 'rollout'")
+    ap.add_argument("--cpu-single-thread", action="store_true",
+                    help="also time the oracle on one thread on the tiny fp32 case and the 480p chunk")
     ap.add_argument("--cpu-sample-qblocks", type=int, default=0, help="0: every query block (the whole call)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one elementwise kernel that reads and writes this many MiB "
@@ -187,7 +189,7 @@ def cpu_baseline(w, x, k_frames, k_blocks, sample_qblocks: int):
     flops = effective_flops(w, s["sel_blocks"], s["n_sel"])
     return {
         "value": float(flops / t_step / 1e12), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"full oracle compress ({t1 - t0:.2f}s) + select ({t2 - t1:.2f}s) of one 480p chunk call; "
+        "sample": (f"full oracle compress ({t1 - t0:.2f}s) + select ({t2 - t1:.2f}s) of one {w.name} call; "
                    f"float64 dense-masked attention on {len(pick)} of {len(all_q)} query blocks "
                    f"({t4 - t3:.2f}s), scaled to all of them; {t_step:.1f}s per call"),
         "s_per_step": t_step,
@@ -456,6 +458,19 @@ def main():
     if args.rollout:
         print("[bench] chunk rollout", file=sys.stderr, flush=True)
         result["rollout"] = rollout(max(args.warmup, 1))
+    if args.cpu_single_thread:
+        # The oracle with BLAS held to one thread: the tiny fp32 case whole, and
+        # the 480p chunk call (compress + select + attention on 150 sampled
+        # query blocks, scaled to all 900).
+        from threadpoolctl import threadpool_limits
+
+        st = {}
+        with threadpool_limits(limits=1):
+            for wl, sample in ((I.TINY_FP32, 0), (I.WAN480P_CHUNK, 150)):
+                xs = I.make_inputs(wl)
+                r = cpu_baseline(wl, xs, wl.k_frames, wl.k_blocks, sample)
+                st[wl.name] = {"s_per_call": round(r["s_per_step"], 4), "sample": r["sample"]}
+        result["cpu_single_thread"] = st
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, host0, w.k_frames, w.k_blocks, args.cpu_sample_qblocks)
