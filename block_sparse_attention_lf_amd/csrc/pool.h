@@ -28,16 +28,21 @@ __device__ inline void unpack16<__bf16>(const uint4& v, float* f) {
   }
 }
 
-// Float64 column sums of `rows` rows of D elements starting at src, reduced
-// across the wavefront: on return every lane holds, for its columns
-// col .. col+EPL-1, the sums over all rows.
-template <typename T, int D>
+// Float64 column sums of `rows` rows, over the DS columns starting at src
+// (rows D elements apart; DS = D for whole rows, less for a column slice),
+// reduced across the wavefront: on return every lane holds, for its columns
+// col .. col+EPL-1 of the slice, the sums over all rows.
+template <typename T, int D, int DS = D>
 struct BlockPool {
   static constexpr int EPL = 16 / (int)sizeof(T);  // elements per 16-byte load
-  static constexpr int LPR = D / EPL;              // lanes per row
+  static constexpr int LPR = DS / EPL;             // lanes per row (slice)
   static constexpr int RPL = 64 / LPR;             // rows per wave-wide load
-  static constexpr int UNROLL = sizeof(T) == 2 ? 16 : 8;  // loads in flight per lane (fits 128 registers)
-  static_assert(64 % LPR == 0, "row must map onto whole lanes");
+  // loads in flight per lane: 16 (bf16) / 8 (f32) for whole rows, which
+  // keeps the registers under 128; a slice takes at most a 64-row block's worth
+  static constexpr int UNROLL_MAX = sizeof(T) == 2 ? 16 : 8;
+  static constexpr int UNROLL_BLOCK = (64 + RPL - 1) / RPL;
+  static constexpr int UNROLL = DS == D || UNROLL_BLOCK > UNROLL_MAX ? UNROLL_MAX : UNROLL_BLOCK;
+  static_assert(64 % LPR == 0 && D % DS == 0, "row slice must map onto whole lanes");
 
   __device__ static void sums(const T* src, int rows, int lane, double (&acc)[EPL]) {
     const int sub = lane / LPR;
