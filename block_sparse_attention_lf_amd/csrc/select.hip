@@ -49,36 +49,68 @@ constexpr int kPerRound = 64 / kDotLanes;
 constexpr int kBlockBatch = 1024;
 static_assert(LF_MAX_BLOCKS_PER_FRAME <= kBlockBatch, "one frame's blocks must fit a batch");
 
-// Dot product of the pooled query (LDS) with key row k, shared by the
-// kDotLanes lanes of one candidate: lane `part` sums d in [part*D/8,
-// (part+1)*D/8) in ascending order, then a butterfly adds the partial sums.
-// Every lane of the group returns the same value (a + b == b + a exactly).
-// All 64 lanes must call it (the butterfly exchanges across lanes).
-template <int D>
-__device__ inline double dot_split(const float* __restrict__ qv_lds, const float* __restrict__ k, int part) {
-  constexpr int SPAN = D / kDotLanes;
-  static_assert(SPAN % 4 == 0, "each lane reads whole float4s");
-  const float* kp = k + part * SPAN;
-  const float* qp = qv_lds + part * SPAN;
-  double acc = 0.0;
-#pragma unroll
-  for (int d = 0; d < SPAN; d += 4) {
-    const float4 kv = *reinterpret_cast<const float4*>(kp + d);
-    acc = fma((double)qp[d], (double)kv.x, acc);
-    acc = fma((double)qp[d + 1], (double)kv.y, acc);
-    acc = fma((double)qp[d + 2], (double)kv.z, acc);
-    acc = fma((double)qp[d + 3], (double)kv.w, acc);
-  }
-#pragma unroll
-  for (int m = 1; m < kDotLanes; m <<= 1) acc += __shfl_xor(acc, m);
-  return acc;
+// v of another lane of the same row of 16 lanes, moved by the DPP control
+// CTRL (a register move between lanes, no LDS round trip), per 32-bit half.
+template <int CTRL>
+__device__ inline double dpp_move(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i of 8 <- lane 7-i
+
+// Dot products of the pooled query with key rows, each shared by the
+// kDotLanes lanes of one candidate: lane `part` sums d in [part*D/8,
+// (part+1)*D/8) in ascending order, then a butterfly adds the partial sums:
+// pairs (lane ^ 1), then (lane ^ 2), then the two quads of the group (after
+// two steps all lanes of a quad hold the same value, so the mirrored lane
+// stands for its quad). Every lane of the group returns the same value
+// (a + b == b + a exactly). All 64 lanes must take part (lanes exchange
+// values). The lane's slice of the query lives in registers (QSlice); the
+// key slices of several candidates are loaded before any is summed, so one
+// memory round trip serves several rounds.
+template <int D>
+struct QSlice {
+  static constexpr int SPAN = D / kDotLanes;
+  static_assert(SPAN % 4 == 0, "each lane reads whole float4s");
+  double q[SPAN];
+  __device__ void load(const float* __restrict__ qv_lds, int part) {
+#pragma unroll
+    for (int d = 0; d < SPAN; ++d) q[d] = (double)qv_lds[part * SPAN + d];
+  }
+  // this lane's slice of key row k
+  __device__ static void load_key(const float* __restrict__ k, int part, float4 (&kv)[SPAN / 4]) {
+#pragma unroll
+    for (int t = 0; t < SPAN / 4; ++t) kv[t] = *reinterpret_cast<const float4*>(k + part * SPAN + 4 * t);
+  }
+  __device__ double dot(const float4 (&kv)[SPAN / 4]) const {
+    double acc = 0.0;
+#pragma unroll
+    for (int t = 0; t < SPAN / 4; ++t) {
+      acc = fma(q[4 * t], (double)kv[t].x, acc);
+      acc = fma(q[4 * t + 1], (double)kv[t].y, acc);
+      acc = fma(q[4 * t + 2], (double)kv[t].z, acc);
+      acc = fma(q[4 * t + 3], (double)kv[t].w, acc);
+    }
+    static_assert(kDotLanes == 8, "the butterfly below covers groups of 8 lanes");
+    acc += dpp_move<kDppXor1>(acc);
+    acc += dpp_move<kDppXor2>(acc);
+    acc += dpp_move<kDppHalfMirror>(acc);
+    return acc;
+  }
+};
+// Rounds of kPerRound candidates whose key slices are in flight together.
+constexpr int kRoundsInFlight = 4;
 
 // keep[c] = 1 iff fewer than k candidates rank above c.
 __device__ inline void rank_keep(const double* score, int n, int k, unsigned char* keep, int lane) {
   for (int c = lane; c < n; c += 64) {
     const double s = score[c];
     int above = 0;
+#pragma unroll 8
     for (int i = 0; i < n; ++i) {
       const double t = score[i];
       above += (t > s) || (t == s && i < c);
@@ -138,13 +170,29 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
   for (int i = lane; i < ns * nb; i += 64) out[i] = i;  // sink frames in full
   int pos = ns * nb;
 
-  // Stage 1: frame scores (kPerRound candidates per round; lanes past the
-  // last candidate recompute the last one and drop it).
+  QSlice<D> qs;
+  qs.load(qv, part);
+  constexpr int KV = QSlice<D>::SPAN / 4;
+
+  // Stage 1: frame scores (kPerRound candidates per round, kRoundsInFlight
+  // rounds loaded at once; lanes past the last candidate recompute the last
+  // one and drop it).
   const int ncand = g.Fh - ns;
-  for (int r0 = 0; r0 < ncand; r0 += kPerRound) {
-    const int c = r0 + sub;
-    const double sc = dot_split<D>(qv, k_frm + key_row(FUSED, g, bh, ns + min(c, ncand - 1)) * D, part);
-    if (c < ncand && part == 0) fscore[c] = sc;
+  for (int r0 = 0; r0 < ncand; r0 += kPerRound * kRoundsInFlight) {
+    float4 kv[kRoundsInFlight][KV];
+#pragma unroll
+    for (int u = 0; u < kRoundsInFlight; ++u) {
+      if (r0 + u * kPerRound >= ncand) break;  // uniform: the whole wavefront skips
+      const int c = min(r0 + u * kPerRound + sub, ncand - 1);
+      QSlice<D>::load_key(k_frm + key_row(FUSED, g, bh, ns + c) * D, part, kv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRoundsInFlight; ++u) {
+      if (r0 + u * kPerRound >= ncand) break;
+      const int c = r0 + u * kPerRound + sub;
+      const double sc = qs.dot(kv[u]);
+      if (c < ncand && part == 0) fscore[c] = sc;
+    }
   }
   __syncthreads();
   rank_keep(fscore, ncand, kf, fkeep, lane);
@@ -167,12 +215,22 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
     if (nbf == 0) break;
     __syncthreads();  // bframe is visible
     const int nc = nbf * nb;
-    for (int r0 = 0; r0 < nc; r0 += kPerRound) {
-      const int x = r0 + sub, xc = min(x, nc - 1);
-      const int fi = xc / nb, j = xc - fi * nb;
-      const float* row = k_blk + (key_row(FUSED, g, bh, bframe[fi]) * nb + j) * (int64_t)D;
-      const double sc = dot_split<D>(qv, row, part);
-      if (x < nc && part == 0) bscore[x] = sc;
+    for (int r0 = 0; r0 < nc; r0 += kPerRound * kRoundsInFlight) {
+      float4 kv[kRoundsInFlight][KV];
+#pragma unroll
+      for (int u = 0; u < kRoundsInFlight; ++u) {
+        if (r0 + u * kPerRound >= nc) break;  // uniform: the whole wavefront skips
+        const int xc = min(r0 + u * kPerRound + sub, nc - 1);
+        const int fi = xc / nb, j = xc - fi * nb;
+        QSlice<D>::load_key(k_blk + (key_row(FUSED, g, bh, bframe[fi]) * nb + j) * (int64_t)D, part, kv[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kRoundsInFlight; ++u) {
+        if (r0 + u * kPerRound >= nc) break;
+        const int x = r0 + u * kPerRound + sub;
+        const double sc = qs.dot(kv[u]);
+        if (x < nc && part == 0) bscore[x] = sc;
+      }
     }
     __syncthreads();
     for (int x = lane; x < nc; x += 64) {  // rank inside the candidate's frame
@@ -180,6 +238,7 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
       const double* seg = bscore + fi * nb;
       const double sc = seg[j];
       int above = 0;
+#pragma unroll 8
       for (int i = 0; i < nb; ++i) {
         const double t = seg[i];
         above += (t > sc) || (t == sc && i < j);
