@@ -15,9 +15,11 @@
 // descending, take the first k" without sorting.
 //
 // Design: one wavefront per (batch, head, query block). Each dot product is
-// shared by 8 lanes (the pooled query is broadcast from LDS), so a wavefront
+// shared by 8 lanes (each holds its D/8 channels of the pooled query in
+// registers; the partial sums meet through DPP lane moves), so a wavefront
 // scores 8 candidates per round with dependent chains of D/8 fused
-// multiply-adds. The frame candidates are scored, ranked against the scores
+// multiply-adds, and the key slices of four rounds are loaded before any is
+// summed. The frame candidates are scored, ranked against the scores
 // kept in LDS, and then the blocks of all kept frames are scored as one batch
 // (up to 1024 at a time) and ranked inside their frame; kept ids are
 // compacted in ascending order with a ballot and a prefix popcount. The whole
