@@ -493,14 +493,6 @@ def chunk_budget(sigma: Sequence[float], weight: Sequence[float], dense: Sequenc
     return {"beta": beta, "sparsity": s, "k_frames": kf, "k_blocks": kb}
 
 
-def achieved_sparsity(hist_frames: int, n_sink: int, blocks_per_frame: int, k_frames: int, k_blocks: int) -> float:
-    """Fraction of history blocks a query block does not attend."""
-    total = hist_frames * blocks_per_frame
-    if total == 0:
-        return 0.0
-    return 1.0 - max_selected(hist_frames, n_sink, blocks_per_frame, k_frames, k_blocks) / total
-
-
 # ---------------------------------------------------------------------------
 # KV cache slot table (Self Forcing rolling cache; Rolling Forcing anchors)
 # ---------------------------------------------------------------------------

@@ -59,3 +59,37 @@ def test_quantiser_round_trip_error_is_within_half_an_e4m3_step():
     step = O.e8m0_decode(scales)[..., None]
     bound = np.maximum(np.abs(x.reshape(4, 6, 4, 32)) * 2.0 ** -4, step * 2.0 ** -10)
     assert np.all(err <= bound * (1 + 1e-12))
+
+
+def _torch_e4m3(rng, shape):
+    """Random E4M3 codes and their values, decoded by torch's float8_e4m3fn (not by the oracle)."""
+    x = torch.from_numpy(rng.standard_normal(shape) * 3.0).to(torch.float8_e4m3fn)
+    return x.view(torch.uint8).numpy().copy(), x.to(torch.float64).numpy()
+
+
+def test_attention_fp8_is_attention_on_the_values_the_codes_stand_for():
+    """attention_fp8(codes, scales) = attention(values) where each value is a torch-decoded E4M3 code times
+    2^(scale code - 127) of its own 32-channel block. Scales differ per token and per block, and q's differ
+    from k's, so using one tensor's scales for the other, a wrong block width, or decoding V as codes all
+    change the result; V is passed as plain values."""
+    w = I.TINY_FP32.replace(head_dim=64, seed=3)
+    x = I.make_inputs(w)
+    rng = np.random.default_rng(7)
+    q8, qv = _torch_e4m3(rng, x["q"].shape)
+    k8, kv = _torch_e4m3(rng, x["k_cache"].shape)
+    qs = rng.integers(124, 131, size=x["q"].shape[:-1] + (2,), dtype=np.uint8)
+    ks = rng.integers(121, 128, size=x["k_cache"].shape[:-1] + (2,), dtype=np.uint8)
+    q_val = qv * np.repeat(np.exp2(qs.astype(np.float64) - 127.0), 32, axis=-1)
+    k_val = kv * np.repeat(np.exp2(ks.astype(np.float64) - 127.0), 32, axis=-1)
+    c = O.compress(x["q"], x["k_cache"], x["frame_slot"], w.tokens_per_frame, w.block, w.chunk_frames, w.hist_frames)
+    s = O.select(c["q_blk"], c["k_blk"], c["k_frm"], w.hist_frames, w.n_sink, w.blocks_per_frame, w.k_frames,
+                 w.k_blocks)
+    args = (x["v_cache"], x["frame_slot"], s["sel_blocks"], s["n_sel"], w.tokens_per_frame, w.block, w.chunk_frames,
+            w.hist_frames, 0.125)
+    want = O.attention(q_val, k_val, *args)
+    got = O.attention_fp8(q8, qs, k8, ks, *args)
+    np.testing.assert_allclose(got["out"], want["out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got["lse"], want["lse"], rtol=0, atol=1e-12)
+    # the pin has power: the same codes with every q scale one step up is a different attention
+    other = O.attention_fp8(q8, qs + 1, k8, ks, *args)
+    assert np.abs(other["out"] - want["out"]).max() > 1e-3
