@@ -122,6 +122,22 @@ def sample_qblocks(w: I.Workload, n_random: int = 4, seed: int = 0):
     return [(b, h, qb) for b in batches for h in heads for qb in sorted(picks)]
 
 
+def sample_every_head(w: I.Workload, per_head: int = 2, seed: int = 0):
+    """Query blocks covering every (batch, head): per head `per_head` spread query blocks (a different
+    residue of the head's query blocks each time), and the first and the last three query blocks of every
+    head, where ragged frames and work-list tails sit."""
+    rng = np.random.default_rng(seed)
+    nqb = w.n_qblocks
+    out = []
+    for b in range(w.batch):
+        for h in range(w.heads):
+            picks = {0, max(nqb - 3, 0), max(nqb - 2, 0), nqb - 1}
+            picks |= set(int(v) for v in rng.integers(0, nqb, per_head))
+            picks.add((h * 7 + b) % nqb)
+            out += [(b, h, qb) for qb in sorted(picks)]
+    return out
+
+
 def qblock_rows(w: I.Workload, qb: int):
     fc, j = divmod(qb, w.blocks_per_frame)
     s = fc * w.tokens_per_frame + j * w.block

@@ -115,21 +115,21 @@ def test_fp8_sharp_logits():
     _run(_odd(200, 64), scale_mult=8.0)
 
 
-def test_fp8_wan480p_chunk_sampled():
-    """The 480p chunk at full size (12 heads, 4680 queries, 6 history frames), sampled query blocks."""
-    w = I.WAN480P_CHUNK
-    _run(w, qblocks=P.sample_qblocks(w))
+def test_fp8_wan480p_chunk_every_row():
+    """The 480p chunk at full size (12 heads, 4680 queries, 6 history frames), every query block."""
+    _run(I.WAN480P_CHUNK)
 
 
-def test_fp8_wide_head_sampled():
-    """40 heads, 3600-token frames, 128-token blocks (double-buffered walk), sampled query blocks."""
+def test_fp8_wide_head_every_head():
+    """40 heads, 3600-token frames, 128-token blocks: the first and last three and spread query blocks of
+    every head."""
     w = I.WIDE_HEAD
-    _run(w, qblocks=P.sample_qblocks(w, n_random=2))
+    _run(w, qblocks=P.sample_every_head(w, per_head=1))
 
 
-def test_fp8_long_history_sink_sampled():
+def test_fp8_long_history_sink_every_head():
     w = I.LONG_HISTORY_SINK
-    _run(w, qblocks=P.sample_qblocks(w, n_random=2))
+    _run(w, qblocks=P.sample_every_head(w, per_head=1))
 
 
 def test_fp8_selection_lists_near_lf_max_sel():

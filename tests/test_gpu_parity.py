@@ -4,8 +4,11 @@ Every test draws seeded inputs, runs lf_compress / lf_select /
 lf_block_sparse_attn on the GPU and the oracle on the CPU, and compares:
 pooled vectors bit-exact, selected ids bit-exact up to score ties within
 1e-5 relative, attention (given the oracle's mask) within max-abs 2e-2,
-mean-abs 2e-3 and relative L2 1e-2. Full-size workloads are compared on all
-query blocks for pooling/selection and on sampled query blocks for attention.
+mean-abs 2e-3 and relative L2 1e-2. Pooling and selection are compared on
+every query block of every workload; attention on every query block of the
+480p chunk, the long-history case and every rollout chunk at step 0, and on
+the wide-head case on every head (its first and last three query blocks plus
+spread ones).
 """
 import math
 import sys
@@ -27,7 +30,8 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _full_check(w, x=None, k_frames=None, k_blocks=None, all_rows=False, n_random=4, scale_mult=1.0):
+def _full_check(w, x=None, k_frames=None, k_blocks=None, all_rows=False, n_random=4, scale_mult=1.0,
+                every_head=False):
     k_frames = w.k_frames if k_frames is None else k_frames
     k_blocks = w.k_blocks if k_blocks is None else k_blocks
     _say(f"[parity] {w.name} B={w.batch} H={w.heads} d={w.head_dim} T={w.tokens_per_frame} b={w.block} "
@@ -40,7 +44,7 @@ def _full_check(w, x=None, k_frames=None, k_blocks=None, all_rows=False, n_rando
     assert not bad, f"{len(bad)} of {n} selections differ without a tie, first: {bad[0]}"
     scale = scale_mult / math.sqrt(w.head_dim)
     qbs = ([(b, h, qb) for b in range(w.batch) for h in range(w.heads) for qb in range(w.n_qblocks)]
-           if all_rows else P.sample_qblocks(w, n_random))
+           if all_rows else (P.sample_every_head(w) if every_head else P.sample_qblocks(w, n_random)))
     out, lse = P.gpu_attention(w, g, dev, x, s["sel_blocks"], s["n_sel"], scale)
     stats = P.compare_attention(w, x, out, lse, s["sel_blocks"], s["n_sel"], scale, qbs)
     _say(f"[parity] {w.name}: selections {n} ({excused} tie-excused), attention {stats}")
@@ -57,17 +61,21 @@ def test_tiny_fp32_all_rows():
     _full_check(I.TINY_FP32, all_rows=True)
 
 
-@pytest.mark.parametrize("name", [I.WAN480P_CHUNK.name, I.LONG_HISTORY_SINK.name, I.WIDE_HEAD.name])
-def test_full_size_workloads(name):
-    _full_check(I.WORKLOADS[name], n_random=6)
+@pytest.mark.parametrize("name", [I.WAN480P_CHUNK.name, I.LONG_HISTORY_SINK.name])
+def test_full_size_workloads_every_row(name):
+    _full_check(I.WORKLOADS[name], all_rows=True)
+
+
+def test_wide_head_every_head():
+    _full_check(I.WIDE_HEAD, every_head=True)
 
 
 def test_wan480p_unit_normal_logits():
     """Same shapes with N(0,1) inputs: logits of std ~1, so the softmax is far from uniform."""
-    _full_check(I.WAN480P_CHUNK.replace(dist="normal", seed=11), n_random=6)
+    _full_check(I.WAN480P_CHUNK.replace(dist="normal", seed=11), all_rows=True)
 
 
-@pytest.mark.parametrize("chunk,step", [(0, 0), (1, 0), (3, 3), (6, 1)])
+@pytest.mark.parametrize("chunk,step", [(c, 0) for c in range(7)] + [(3, 3), (6, 1)])
 def test_chunk_rollout(chunk, step):
     r = I.CHUNK_ROLLOUT
     n = r.n_chunks
@@ -75,7 +83,7 @@ def test_chunk_rollout(chunk, step):
                              [r.chunk_frames * i for i in range(n)], None, r.blocks_per_frame, r.k_frames_min)
     kf, kb = bud["k_frames"][chunk], bud["k_blocks"][chunk]
     x = I.rollout_chunk_inputs(r, chunk, step, k_frames=kf, k_blocks=kb)
-    _full_check(x.pop("workload"), x=x, k_frames=kf, k_blocks=kb, n_random=3)
+    _full_check(x.pop("workload"), x=x, k_frames=kf, k_blocks=kb, all_rows=(step == 0), n_random=3)
 
 
 def test_planted_structure_is_recovered():
@@ -199,4 +207,16 @@ def test_selection_lists_at_lf_max_sel(d, T, b, Fh, kb):
                    hist_frames=Fh, n_sink=0, cache_slots=Fh + 1, dtype="bf16", k_frames=Fh, k_blocks=kb,
                    sparsity=float("nan"), seed=12, dist="normal", chunk_index=Fh)
     assert lf.lf_max_sel(lf.geom_of(w), Fh, kb) in (lf.LF_MAX_SEL, lf.LF_MAX_SEL - 4)
+    _full_check(w, all_rows=True)
+
+
+@pytest.mark.parametrize("dtype,H,Fh", [("f32", 16, 8), ("f32", 2, 3), ("bf16", 24, 12)])
+def test_pooling_launch_shapes(dtype, H, Fh):
+    """The pooling launch splits frames into column slices only when that grid gives every workgroup a
+    compute unit of its own, else pools whole frames. Both shapes must give the oracle's bits: (f32, 16
+    heads, 8 frames) is 512 float32 frame slices, beyond the chip's 256 compute units, so whole frames;
+    (f32, 2 heads, 3 frames) takes slices; (bf16, 24 heads, 12 frames) whole frames again."""
+    w = I.Workload(name=f"poolshape_{dtype}_h{H}_f{Fh}", batch=1, heads=H, head_dim=128, grid=(1, 200), block=64,
+                   chunk_frames=1, hist_frames=Fh, n_sink=0, cache_slots=Fh + 1, dtype=dtype, k_frames=2,
+                   k_blocks=2, sparsity=float("nan"), seed=14, dist="normal", chunk_index=Fh)
     _full_check(w, all_rows=True)
