@@ -52,8 +52,9 @@ def parse():
                     help="also time lf_block_sparse_attn_bwd (bf16) and report it under 'backward'")
     ap.add_argument("--fp8", action="store_true",
                     help="also time lf_block_sparse_attn_fp8 (MX-FP8 q/k) on the same selections; report under 'fp8'")
-    ap.add_argument("--rollout", action="store_true",
-                    help="also run the 7-chunk x 4-step rollout (chunk-aware budget per chunk); report under 'rollout'")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline workload (by default the long-history and wide-head workloads "
+                         "and the 7-chunk x 4-step rollout follow, under 'configs' and 'rollout')")
     ap.add_argument("--cpu-single-thread", action="store_true",
                     help="also time the oracle on one thread on the tiny fp32 case and the 480p chunk")
     ap.add_argument("--cpu-sample-qblocks", type=int, default=0, help="0: every query block (the whole call)")
@@ -189,11 +190,183 @@ def cpu_baseline(w, x, k_frames, k_blocks, sample_qblocks: int):
     flops = effective_flops(w, s["sel_blocks"], s["n_sel"])
     return {
         "value": float(flops / t_step / 1e12), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"full oracle compress ({t1 - t0:.2f}s) + select ({t2 - t1:.2f}s) of one {w.name} call; "
                    f"float64 dense-masked attention on {len(pick)} of {len(all_q)} query blocks "
                    f"({t4 - t3:.2f}s), scaled to all of them; {t_step:.1f}s per call"),
         "s_per_step": t_step,
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class Leg:
+    """One workload on the GPU: seeded input sets resident in HBM, the step (host slot table and budget, then
+    compress -> select -> attention, or fused selection -> attention), and its timing."""
+
+    def __init__(self, w, n_sets: int, path: str):
+        import torch
+
+        from block_sparse_attention_lf_amd import inputs as I
+        from block_sparse_attention_lf_amd import lf
+
+        self.torch, self.lf, self.w, self.path = torch, lf, w, path
+        self.g = lf.geom_of(w)
+        self.scale = 1.0 / math.sqrt(w.head_dim)
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        print(f"[bench] workload {w.name}: drawing {n_sets} input set(s)", file=sys.stderr, flush=True)
+        self.sets, self.host0 = [], None
+        for i in range(n_sets):
+            x = I.make_inputs(w, seed=w.seed + 1000 * i)
+            if i == 0:
+                self.host0 = x
+            self.sets.append(tuple(torch.from_numpy(x[k]).to(tdt).cuda() for k in ("q", "k_cache", "v_cache")))
+            del x
+        self.set_bytes = sum(t.numel() * t.element_size() for t in self.sets[0])
+        self.bufs = lf.Buffers(self.g, w.k_frames, w.k_blocks)
+        self.stream = torch.cuda.current_stream()
+        self.slots = self.host_side()
+        assert list(self.slots) == self.host0["frame_slot"].tolist()
+        # effective FLOPs of each input set (selection is deterministic per set)
+        self.flops = []
+        for dev in self.sets:
+            lf.hsa_attention(self.g, *dev, self.slots, self.bufs, self.scale)
+            torch.cuda.synchronize()
+            self.flops.append(effective_flops(w, self.bufs.sel_blocks.cpu().numpy(), self.bufs.n_sel.cpu().numpy()))
+        self.pooled, self.commit_ms = [], None
+        if path == "fused":
+            self._pool_on_commit()
+
+    def host_side(self):
+        # a0: slot table of the cache for this chunk; a6: chunk budget (single call: its own sparsity)
+        w, lf = self.w, self.lf
+        hist, slots, _ = lf.lf_cache_frame_slots(w.policy, w.cache_slots, w.n_sink, w.chunk_frames, w.chunk_index)
+        lf.lf_chunk_budget([1.0], None, [False], w.sparsity, w.sparsity, [hist], [w.n_sink], w.blocks_per_frame,
+                           w.k_frames)
+        return slots
+
+    def _pool_on_commit(self):
+        # the pooled keys of every history frame live in a slot-indexed cache,
+        # filled when the frame is committed (once per frame, not per step)
+        torch, lf, w, g = self.torch, self.lf, self.w, self.g
+        S, nb, d = w.cache_slots, w.blocks_per_frame, w.head_dim
+        hist_slots = [int(x) for x in self.slots[:w.hist_frames]]
+        for q, kc, vc in self.sets:
+            kp = (torch.empty((w.batch, w.heads, S, nb, d), dtype=torch.float32, device="cuda"),
+                  torch.empty((w.batch, w.heads, S, d), dtype=torch.float32, device="cuda"))
+            lf.lf_pool_keys(g, kc, hist_slots, kp[0], kp[1], self.stream)
+            self.pooled.append(kp)
+        # cost of one commit: pooling the chunk's own frames (they become history)
+        chunk_slots = [int(x) for x in self.slots[w.hist_frames:w.hist_frames + w.chunk_frames]]
+        cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        times = []
+        n = len(self.sets)
+        for r in range(6):
+            kc = self.sets[r % n][1]
+            cev[0].record(self.stream)
+            lf.lf_pool_keys(g, kc, chunk_slots, self.pooled[r % n][0], self.pooled[r % n][1], self.stream)
+            cev[1].record(self.stream)
+            torch.cuda.synchronize()
+            times.append(cev[0].elapsed_time(cev[1]))
+        self.commit_ms = float(np.median(times[1:]))
+        for (q, kc, vc), kp in zip(self.sets, self.pooled):  # restore the history pooling the steps read
+            lf.lf_pool_keys(g, kc, hist_slots, kp[0], kp[1], self.stream)
+        torch.cuda.synchronize()
+
+    def step(self, i, ev=None, stage_ev=False):
+        # ev: events around the attention launch (the roofline's kernel time);
+        # stage_ev: two more around the first stage(s), for the stage split only
+        # (each timing event costs the GPU a few microseconds per step, so the
+        # timed steps carry just the two the roofline needs).
+        lf, w, g, bufs, stream = self.lf, self.w, self.g, self.bufs, self.stream
+        q, kc, vc = self.sets[i % len(self.sets)]
+        sl = self.host_side()
+        if stage_ev:
+            ev[0].record(stream)
+        if self.path == "fused":
+            kp_blk, kp_frm = self.pooled[i % len(self.sets)]
+            if stage_ev:
+                ev[1].record(stream)
+            lf.lf_select_fused(g, q, kp_blk, kp_frm, sl, w.k_frames, w.k_blocks, bufs.sel_frames, bufs.sel_blocks,
+                               bufs.n_sel, None, stream)
+        else:
+            lf.lf_compress(g, q, kc, sl, bufs.q_blk, bufs.k_blk, bufs.k_frm, stream)
+            if stage_ev:
+                ev[1].record(stream)
+            lf.lf_select(g, bufs.q_blk, bufs.k_blk, bufs.k_frm, w.k_frames, w.k_blocks, bufs.sel_frames,
+                         bufs.sel_blocks, bufs.n_sel, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        lf.lf_block_sparse_attn(g, q, kc, vc, sl, bufs.sel_blocks, bufs.n_sel, self.scale, bufs.out, None, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    def time(self, steps: int, warmup: int) -> dict:
+        """Exactly `steps` steps between two device synchronisations (after `warmup` untimed ones), HIP events
+        around each attention launch; then a separate pass with events around every stage for the split."""
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        # The cyclic garbage collector is paused inside the timed region: a full
+        # pass over a process holding torch takes tens of milliseconds and would
+        # land in a random step.
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        gc.collect()
+        gc.disable()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i, evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        gc.enable()
+        sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for i in range(steps):
+            self.step(i, sevs[i], stage_ev=True)
+        torch.cuda.synchronize()
+        w = self.w
+        ms_step = (t1 - t0) * 1e3 / steps
+        attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+        first_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in sevs]))
+        sel_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in sevs]))
+        flops = float(np.mean([self.flops[i % len(self.sets)] for i in range(steps)]))
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+        r = {"ms_per_step": ms_step, "attn_ms": attn_ms, "flops": flops, "attn_tflops": attn_tflops,
+             "attn_frac": attn_tflops / peak, "peak": peak, "value": flops / (ms_step * 1e-3) / 1e12,
+             "select_ms": sel_ms}
+        if self.path == "fused":
+            r["stages_ms"] = {"select_fused": sel_ms, "attention": attn_ms}
+        else:
+            cbytes = compress_bytes(w)
+            gbs = cbytes / (first_ms * 1e-3) / 1e9
+            r["stages_ms"] = {"compress": first_ms, "select": sel_ms, "attention": attn_ms}
+            r["compress"] = {"bound": "hbm", "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS,
+                             "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": cbytes}
+        return r
+
+
+def config_summary(leg: "Leg", r: dict, steps: int) -> dict:
+    """Per-workload figures on the bench's own clock (the extra configurations)."""
+    out = {"steps": steps, "input_sets_rotated": len(leg.sets), "ms_per_step": round(r["ms_per_step"], 4),
+           "effective_gflop_per_step": round(r["flops"] / 1e9, 2),
+           "step_tflops": round(r["value"], 1),
+           "attention": {"avg_launch_ms": round(r["attn_ms"], 4), "achieved": round(r["attn_tflops"], 1),
+                         "peak": r["peak"], "unit": "TFLOP/s", "frac": round(r["attn_frac"], 4)},
+           "stages_ms": {k: round(v, 4) for k, v in r["stages_ms"].items()}}
+    if "compress" in r:
+        out["compress"] = r["compress"]
+    return out
 
 
 def main():
@@ -213,169 +386,44 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     w = I.WORKLOADS[args.workload] if args.workload else I.WAN480P_CHUNK
-    g = lf.geom_of(w)
-    scale = 1.0 / math.sqrt(w.head_dim)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    print(f"[bench] workload {w.name}: drawing {N_SETS} input sets", file=sys.stderr, flush=True)
-
-    sets = []
-    host0 = None
-    for i in range(N_SETS):
-        x = I.make_inputs(w, seed=w.seed + 1000 * i)
-        if i == 0:
-            host0 = x
-        dev = tuple(torch.from_numpy(x[k]).to(tdt).cuda() for k in ("q", "k_cache", "v_cache"))
-        sets.append(dev)
-        if i > 0:
-            del x
-    set_bytes = sum(t.numel() * t.element_size() for t in sets[0])
-    bufs = lf.Buffers(g, w.k_frames, w.k_blocks)
-    stream = torch.cuda.current_stream()
-    policy = w.policy
-    n = 1
-
-    def host_side():
-        # a0: slot table of the cache for this chunk; a6: chunk budget (single call: its own sparsity)
-        hist, slots, _ = lf.lf_cache_frame_slots(policy, w.cache_slots, w.n_sink, w.chunk_frames, w.chunk_index)
-        lf.lf_chunk_budget([1.0], None, [False], w.sparsity, w.sparsity, [hist], [w.n_sink], w.blocks_per_frame,
-                           w.k_frames)
-        return slots
-
-    slots = host_side()
-    assert list(slots) == host0["frame_slot"].tolist()
-
-    # Effective FLOPs of each input set (selection is deterministic per set).
-    flops = []
-    for dev in sets:
-        lf.hsa_attention(g, *dev, slots, bufs, scale)
-        torch.cuda.synchronize()
-        flops.append(effective_flops(w, bufs.sel_blocks.cpu().numpy(), bufs.n_sel.cpu().numpy()))
-
-    # Fused path: the pooled keys of every history frame live in a slot-indexed
-    # cache, filled when the frame is committed (once per frame, not per step).
-    pooled = []
-    commit_ms = None
-    if args.path == "fused":
-        S, nb, d = w.cache_slots, w.blocks_per_frame, w.head_dim
-        hist_slots = [int(x) for x in slots[:w.hist_frames]]
-        for q, kc, vc in sets:
-            kp = (torch.empty((w.batch, w.heads, S, nb, d), dtype=torch.float32, device="cuda"),
-                  torch.empty((w.batch, w.heads, S, d), dtype=torch.float32, device="cuda"))
-            lf.lf_pool_keys(g, kc, hist_slots, kp[0], kp[1], stream)
-            pooled.append(kp)
-        # cost of one commit: pooling the chunk's own frames (they become history)
-        chunk_slots = [int(x) for x in slots[w.hist_frames:w.hist_frames + w.chunk_frames]]
-        cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        times = []
-        for r in range(6):
-            kc = sets[r % N_SETS][1]
-            cev[0].record(stream)
-            lf.lf_pool_keys(g, kc, chunk_slots, pooled[r % N_SETS][0], pooled[r % N_SETS][1], stream)
-            cev[1].record(stream)
-            torch.cuda.synchronize()
-            times.append(cev[0].elapsed_time(cev[1]))
-        commit_ms = float(np.median(times[1:]))
-        for (q, kc, vc), kp in zip(sets, pooled):  # restore the history pooling the steps read
-            lf.lf_pool_keys(g, kc, hist_slots, kp[0], kp[1], stream)
-        torch.cuda.synchronize()
-
-    def step(i, ev=None, stage_ev=False):
-        # ev: events around the attention launch (the roofline's kernel time);
-        # stage_ev: two more around the first stage(s), for the stage split only
-        # (each timing event costs the GPU a few microseconds per step, so the
-        # timed steps carry just the two the roofline needs).
-        q, kc, vc = sets[i % N_SETS]
-        sl = host_side()
-        if stage_ev:
-            ev[0].record(stream)
-        if args.path == "fused":
-            kp_blk, kp_frm = pooled[i % N_SETS]
-            if stage_ev:
-                ev[1].record(stream)
-            lf.lf_select_fused(g, q, kp_blk, kp_frm, sl, w.k_frames, w.k_blocks, bufs.sel_frames, bufs.sel_blocks,
-                               bufs.n_sel, None, stream)
-        else:
-            lf.lf_compress(g, q, kc, sl, bufs.q_blk, bufs.k_blk, bufs.k_frm, stream)
-            if stage_ev:
-                ev[1].record(stream)
-            lf.lf_select(g, bufs.q_blk, bufs.k_blk, bufs.k_frm, w.k_frames, w.k_blocks, bufs.sel_frames,
-                         bufs.sel_blocks, bufs.n_sel, stream)
-        if ev is not None:
-            ev[2].record(stream)
-        lf.lf_block_sparse_attn(g, q, kc, vc, sl, bufs.sel_blocks, bufs.n_sel, scale, bufs.out, None, stream)
-        if ev is not None:
-            ev[3].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # Timed region: exactly `steps` steps between two device synchronisations.
-    # The cyclic garbage collector is paused inside it: a full pass over a
-    # process holding torch takes tens of milliseconds and would land in a
-    # random step.
+    leg = Leg(w, N_SETS, args.path)
+    g, scale, slots, bufs, stream = leg.g, leg.scale, leg.slots, leg.bufs, leg.stream
+    host0 = leg.host0
+    sets = leg.sets
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    gc.collect()
-    gc.disable()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gc.enable()
-
-    ms_step = (t1 - t0) * 1e3 / K
-    attn = [e[2].elapsed_time(e[3]) for e in evs]
-    # Stage split, from separate (untimed) steps that carry all four events.
-    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    for i in range(K):
-        step(i, sevs[i], stage_ev=True)
-    torch.cuda.synchronize()
-    comp = [e[0].elapsed_time(e[1]) for e in sevs]
-    sel = [e[1].elapsed_time(e[2]) for e in sevs]
-    flops_mean = float(np.mean([flops[i % N_SETS] for i in range(K)]))
-    attn_ms = float(np.mean(attn))
-    attn_tflops = flops_mean / (attn_ms * 1e-3) / 1e12
-    comp_ms = float(np.mean(comp))
-    cbytes = compress_bytes(w)
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    value = flops_mean / (ms_step * 1e-3) / 1e12
+    r = leg.time(K, args.warmup)
+    ms_step, attn_ms, flops_mean, attn_tflops, peak = r["ms_per_step"], r["attn_ms"], r["flops"], r["attn_tflops"], \
+        r["peak"]
+    value = r["value"]
     src = os.path.join(ROOT, "block_sparse_attention_lf_amd", "csrc", "attention.hip")
     traffic = traffic_from_profiles(src, w.name)
 
     result = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": n, "steps": K,
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1)/sqrt(d) q/k/v; no weights)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "tokens_per_frame": w.tokens_per_frame, "block": w.block, "chunk_frames": w.chunk_frames,
                    "hist_frames": w.hist_frames, "k_frames": w.k_frames, "k_blocks": w.k_blocks,
                    "sparsity": w.sparsity, "input_sets_rotated": N_SETS, "path": args.path,
-                   "bytes_per_input_set": int(set_bytes)},
-        "roofline": {"bound": "mfma", "kernel": "attn_kernel (lf_block_sparse_attn)",
+                   "bytes_per_input_set": int(leg.set_bytes)},
+        "roofline": {"bound": "mfma", "kernel": "attn_group_kernel (lf_block_sparse_attn)",
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": flops_mean, "avg_launch_ms": round(attn_ms, 4)},
-        "stages_ms": {"compress": round(comp_ms, 4), "select": round(float(np.mean(sel)), 4),
-                      "attention": round(attn_ms, 4)},
-        "compress": {"bound": "hbm", "achieved_gbs": round(cbytes / (comp_ms * 1e-3) / 1e9, 1),
-                     "peak_gbs": PEAK_HBM_GBS, "frac": round(cbytes / (comp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                     "algorithmic_bytes": cbytes},
+        "stages_ms": {k: round(v, 4) for k, v in r["stages_ms"].items()},
         "attention_pct_of_mfma_peak": round(100 * attn_tflops / peak, 2),
     }
+    if "compress" in r:
+        result["compress"] = r["compress"]
     if args.path == "fused":
-        # one stage: query pooling + selection; history pooling is paid on commit
-        result["stages_ms"] = {"select_fused": round(float(np.mean(sel)), 4), "attention": round(attn_ms, 4)}
-        result.pop("compress")
-        result["pool_on_commit"] = {"ms_per_commit": round(commit_ms, 4), "frames_per_commit": w.chunk_frames}
+        result["pool_on_commit"] = {"ms_per_commit": round(leg.commit_ms, 4), "frames_per_commit": w.chunk_frames}
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 2
-        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
-        dst = torch.empty_like(src)
+        src_t = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src_t)
         torch.cuda.synchronize()
-        torch.neg(src, out=dst)  # reads and writes exactly n bf16 values
+        torch.neg(src_t, out=dst)  # reads and writes exactly n bf16 values
         torch.cuda.synchronize()
         result["calibration_copy_bytes_each_way"] = n * 2
     if args.backward and w.dtype == "bf16":
@@ -454,8 +502,23 @@ def main():
                          "peak": round(fpeak, 1), "unit": "TFLOP/s", "frac": round(fach / fpeak, 4),
                          "frac_of_bf16_peak": round(fach / PEAK_BF16_TFLOPS, 4),
                          "speedup_vs_bf16_attention": round(attn_ms / fms, 3),
-                         "kernel": "attn_kernel Q8 (lf_block_sparse_attn_fp8)"}
-    if args.rollout:
+                         "kernel": "attn_group_kernel Q8 (lf_block_sparse_attn_fp8)"}
+    if not args.headline_only:
+        # The other workloads on the same clock: long history with a sink and the
+        # wide-head case (one input set each beyond what the MALL holds), then
+        # the chunk-wise rollout. Each leg frees its inputs before the next.
+        del leg, sets, bufs
+        torch.cuda.empty_cache()
+        extra = {}
+        for wl, n_sets, steps in ((I.LONG_HISTORY_SINK, 2, 10), (I.WIDE_HEAD, 1, 5)):
+            if wl.name == w.name:
+                continue
+            lg = Leg(wl, n_sets, args.path)
+            rr = lg.time(steps, 2)
+            extra[wl.name] = config_summary(lg, rr, steps)
+            del lg
+            torch.cuda.empty_cache()
+        result["configs"] = extra
         print("[bench] chunk rollout", file=sys.stderr, flush=True)
         result["rollout"] = rollout(max(args.warmup, 1))
     if args.cpu_single_thread:
@@ -468,8 +531,8 @@ def main():
         with threadpool_limits(limits=1):
             for wl, sample in ((I.TINY_FP32, 0), (I.WAN480P_CHUNK, 150)):
                 xs = I.make_inputs(wl)
-                r = cpu_baseline(wl, xs, wl.k_frames, wl.k_blocks, sample)
-                st[wl.name] = {"s_per_call": round(r["s_per_step"], 4), "sample": r["sample"]}
+                rr = cpu_baseline(wl, xs, wl.k_frames, wl.k_blocks, sample)
+                st[wl.name] = {"s_per_call": round(rr["s_per_step"], 4), "sample": rr["sample"]}
         result["cpu_single_thread"] = st
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -30,6 +30,6 @@ def test_a_multi_rank_launch_is_refused_too():
 def test_help_lists_the_options():
     r = _bench("--help")
     assert r.returncode == 0
-    for opt in ("--gpus", "--steps", "--warmup", "--workload", "--path", "--backward", "--fp8", "--rollout",
+    for opt in ("--gpus", "--steps", "--warmup", "--workload", "--path", "--backward", "--fp8", "--headline-only",
                 "--cpu-single-thread", "--cpu-sample-qblocks", "--no-cpu-baseline", "--calibrate-copy-mib"):
         assert opt in r.stdout, opt
