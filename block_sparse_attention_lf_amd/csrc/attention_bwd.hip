@@ -26,6 +26,8 @@
 //   Each key row's gradient is summed inside one workgroup: no atomics, and
 //   every gradient row of a frame named by the slot table is written once
 //   (zero where no query sees it). Rows of other slots are not written.
+#include <mutex>
+
 #include "mfma.h"
 
 namespace lf {
@@ -586,6 +588,33 @@ hipError_t launch_bwd_d(const KGeom& g, const void* q, const void* k, const void
 }
 
 }  // namespace
+
+// Row scratch (delta) of lf_block_sparse_attn_bwd_noalloc: a fixed array in
+// each GPU's copy of the library, LF_NOALLOC_MAX_ROWS floats. Host code never
+// uses its name as an address (on the host the name is a stand-in, not the
+// device address): the address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+static __device__ __align__(256) float scratch[LF_NOALLOC_MAX_ROWS];
+
+hipError_t noalloc_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static float* addr[kMaxDevices];
+  static hipError_t status[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev]() {
+    void* p = nullptr;
+    status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    addr[dev] = static_cast<float*>(p);
+  });
+  if (status[dev] != hipSuccess) return status[dev];
+  if (addr[dev] == nullptr) return hipErrorInvalidSymbol;
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_attention_bwd(const KGeom& g, const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel, float scale,

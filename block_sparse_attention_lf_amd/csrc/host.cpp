@@ -281,6 +281,23 @@ lf_status lf_block_sparse_attn_bwd(const lf_geom* g, const void* q, const void* 
                     "lf_block_sparse_attn_bwd launch");
 }
 
+lf_status lf_block_sparse_attn_bwd_noalloc(const lf_geom* g, const void* q, const void* k_cache,
+                                           const void* v_cache, const int32_t* frame_slot, const int32_t* sel_blocks,
+                                           const int32_t* n_sel, int32_t max_sel, float softmax_scale,
+                                           const void* out, const float* lse, const void* dout, float* dq,
+                                           float* dk_cache, float* dv_cache, lf_stream stream) {
+  if (g == nullptr) return fail(LF_ERR_NULL, "geometry is NULL");
+  const int64_t rows = (int64_t)g->batch * g->heads * g->chunk_frames * g->tokens_per_frame;
+  if (g->batch >= 1 && g->heads >= 1 && g->chunk_frames >= 1 && g->tokens_per_frame >= 1 &&
+      rows > LF_NOALLOC_MAX_ROWS)
+    return fail(LF_ERR_GEOM, "B*H*Fc*T exceeds LF_NOALLOC_MAX_ROWS (the fixed row scratch)");
+  float* delta = nullptr;
+  const hipError_t e = lf::noalloc_scratch(&delta);
+  if (e != hipSuccess) return hip_status(e, "lf_block_sparse_attn_bwd_noalloc: device address of the row scratch");
+  return lf_block_sparse_attn_bwd(g, q, k_cache, v_cache, frame_slot, sel_blocks, n_sel, max_sel, softmax_scale, out,
+                                  lse, dout, delta, dq, dk_cache, dv_cache, stream);
+}
+
 lf_status lf_chunk_budget(int32_t n_chunks, const double* sigma, const double* weight, const uint8_t* dense,
                           double s_base, double s_target, const int32_t* hist_frames, const int32_t* n_sink,
                           int32_t blocks_per_frame, int32_t k_frames_min, double* sparsity_out, double* beta_out,

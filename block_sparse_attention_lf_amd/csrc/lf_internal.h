@@ -51,4 +51,8 @@ hipError_t launch_attention_bwd(const KGeom& g, const void* q, const void* k_cac
                                 const void* out, const float* lse, const void* dout, float* delta, float* dq,
                                 float* dk_cache, float* dv_cache, hipStream_t stream);
 
+// Device address of the fixed row scratch of the allocation-free backward on
+// the current device (looked up once per device); hipSuccess or the lookup's error.
+hipError_t noalloc_scratch(float** ptr);
+
 }  // namespace lf

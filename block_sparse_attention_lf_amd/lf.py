@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(HERE, "liblf.so")
 LF_F32, LF_BF16 = 0, 1
 LF_CACHE_ROLLING, LF_CACHE_ANCHORED = 0, 1
 LF_MAX_FRAMES, LF_MAX_BLOCKS_PER_FRAME, LF_MAX_BLOCK, LF_MAX_SEL, LF_MAX_CANDIDATES_1D = 256, 512, 128, 512, 4096
+LF_NOALLOC_MAX_ROWS = 1 << 20
 LF_MAX_CACHE_SLOTS = 16384
 
 STATUS = {0: "LF_OK", -1: "LF_ERR_NULL", -2: "LF_ERR_GEOM", -3: "LF_ERR_DTYPE", -4: "LF_ERR_K",
@@ -30,7 +31,8 @@ STATUS = {0: "LF_OK", -1: "LF_ERR_NULL", -2: "LF_ERR_GEOM", -3: "LF_ERR_DTYPE", 
 
 # Every symbol include/lf.h declares.
 EXPORTS = ("lf_compress", "lf_max_sel", "lf_select", "lf_max_sel_1d", "lf_select_blocks", "lf_pool_keys", "lf_select_fused", "lf_block_sparse_attn",
-           "lf_block_sparse_attn_fp8", "lf_block_sparse_attn_bwd", "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error")
+           "lf_block_sparse_attn_fp8", "lf_block_sparse_attn_bwd", "lf_block_sparse_attn_bwd_noalloc",
+           "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error")
 
 
 class LfError(RuntimeError):
@@ -86,6 +88,8 @@ def lib() -> ctypes.CDLL:
                                                     ctypes.c_float, _P, _P, _P]),
         "lf_block_sparse_attn_bwd": (ctypes.c_int, [G, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32, ctypes.c_float,
                                                     _P, _P, _P, _P, _P, _P, _P, _P]),
+        "lf_block_sparse_attn_bwd_noalloc": (ctypes.c_int, [G, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32,
+                                                            ctypes.c_float, _P, _P, _P, _P, _P, _P, _P]),
         "lf_chunk_budget": (ctypes.c_int, [ctypes.c_int32, _F64P, _F64P, ctypes.POINTER(ctypes.c_uint8),
                                            ctypes.c_double, ctypes.c_double, _I32P, _I32P, ctypes.c_int32,
                                            ctypes.c_int32, _F64P, _F64P, _I32P, _I32P]),
@@ -298,6 +302,32 @@ def lf_block_sparse_attn_bwd(g: lf_geom, q, k_cache, v_cache, frame_slot, sel_bl
                                           _ptr(sel_blocks), _ptr(n_sel), max_sel, float(softmax_scale), _ptr(out),
                                           _ptr(lse), _ptr(dout), _ptr(delta), _ptr(dq), _ptr(dk_cache),
                                           _ptr(dv_cache), _stream(stream)), "lf_block_sparse_attn_bwd")
+
+
+def lf_block_sparse_attn_bwd_noalloc(g: lf_geom, q, k_cache, v_cache, frame_slot, sel_blocks, n_sel,
+                                     softmax_scale: float, out, lse, dout, dq, dk_cache, dv_cache, stream=None) -> None:
+    """lf_block_sparse_attn_bwd with its row scratch in the library's fixed device array (see include/lf.h):
+    allocates nothing; calls that overlap on one GPU race."""
+    D = g.head_dim
+    _need(q, (g.batch, g.heads, g.q_len, D), torch.bfloat16, "q")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, (g.batch, g.heads, g.cache_slots, g.tokens_per_frame, D), torch.bfloat16, name)
+    for name, t in (("out", out), ("dout", dout)):
+        _need(t, (g.batch, g.heads, g.q_len, D), torch.bfloat16, name)
+    _need(lse, (g.batch, g.heads, g.q_len), torch.float32, "lse")
+    _need(dq, (g.batch, g.heads, g.q_len, D), torch.float32, "dq")
+    for name, t in (("dk_cache", dk_cache), ("dv_cache", dv_cache)):
+        _need(t, (g.batch, g.heads, g.cache_slots, g.tokens_per_frame, D), torch.float32, name)
+    max_sel = 0 if sel_blocks is None else sel_blocks.shape[-1]
+    if sel_blocks is not None:
+        _need(sel_blocks, (g.batch, g.heads, g.n_qblocks, max_sel), torch.int32, "sel_blocks")
+        _need(n_sel, (g.batch, g.heads, g.n_qblocks), torch.int32, "n_sel")
+    arr, sp = _slots(frame_slot)
+    _check(lib().lf_block_sparse_attn_bwd_noalloc(ctypes.byref(g), _ptr(q), _ptr(k_cache), _ptr(v_cache), sp,
+                                                  _ptr(sel_blocks), _ptr(n_sel), max_sel, float(softmax_scale),
+                                                  _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk_cache),
+                                                  _ptr(dv_cache), _stream(stream)),
+           "lf_block_sparse_attn_bwd_noalloc")
 
 
 def lf_chunk_budget(sigma, weight, dense, s_base: float, s_target: float, hist_frames, n_sink, blocks_per_frame: int,

@@ -45,7 +45,13 @@
  *   - Errors: arguments are validated on the host before anything is
  *     enqueued. A failing call returns a negative lf_status and enqueues
  *     nothing. LF_ERR_HIP reports a launch failure; lf_last_error() gives the
- *     detail string (per thread). There is no other global state.
+ *     detail string (per thread).
+ *   - Global state: besides that per-thread string, a per-device cache of the
+ *     compute-unit count (filled once, read-only after) and the per-device
+ *     row scratch of lf_block_sparse_attn_bwd_noalloc (its address looked up
+ *     once per device). Every entry point is safe to call from several host
+ *     threads; only lf_block_sparse_attn_bwd_noalloc calls that overlap on
+ *     one GPU share memory (its scratch).
  *
  * One attention call of one layer at one denoise step of a chunk:
  *   lf_cache_frame_slots(policy, S, n_sink, Fc, chunk, &Fh, frame_slot, ids);
@@ -98,6 +104,9 @@ typedef enum { LF_CACHE_ROLLING = 0, LF_CACHE_ANCHORED = 1 } lf_cache_policy;
 #define LF_MAX_SEL 512
 /* Most candidate blocks ((Fh - n_sink) * nb) the single-level selection ranks. */
 #define LF_MAX_CANDIDATES_1D 4096
+/* Most query rows (B * H * Fc * T) lf_block_sparse_attn_bwd_noalloc takes:
+ * its row scratch is a fixed device array of this many floats (4 MiB). */
+#define LF_NOALLOC_MAX_ROWS (1 << 20)
 
 typedef struct {
   int32_t batch;            /* B >= 1 */
@@ -246,6 +255,26 @@ lf_status lf_block_sparse_attn_bwd(const lf_geom* g, const void* q, const void* 
                                    int32_t max_sel, float softmax_scale, const void* out, const float* lse,
                                    const void* dout, float* delta, float* dq, float* dk_cache, float* dv_cache,
                                    lf_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * lf_block_sparse_attn_bwd without the delta argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). The row scratch (delta) lives in
+ * a fixed array of LF_NOALLOC_MAX_ROWS floats in the library's device memory,
+ * one per GPU, held until the process ends; its address is looked up once per
+ * device at the first call on it. The call allocates nothing.
+ * Arguments, outputs and errors as lf_block_sparse_attn_bwd; in addition
+ * B * H * Fc * T > LF_NOALLOC_MAX_ROWS returns LF_ERR_GEOM, and a failed
+ * lookup of the scratch returns LF_ERR_HIP. Calls on one GPU share its
+ * scratch: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller. Every row of the scratch a
+ * call reads it has written before, so nothing needs clearing.
+ * ------------------------------------------------------------------------- */
+lf_status lf_block_sparse_attn_bwd_noalloc(const lf_geom* g, const void* q, const void* k_cache,
+                                           const void* v_cache, const int32_t* frame_slot, const int32_t* sel_blocks,
+                                           const int32_t* n_sel, int32_t max_sel, float softmax_scale,
+                                           const void* out, const float* lse, const void* dout, float* dq,
+                                           float* dk_cache, float* dv_cache, lf_stream stream);
 
 /* ---------------------------------------------------------------------------
  * Chunk-aware growth budget ([LF-tech] 2.1; [LF-press] 2). Host only.
