@@ -38,7 +38,8 @@
 //   * Online softmax in fp32 with exp2 (scale folded into log2(e) units)
 //     against the running maximum, without a per-tile maximum; a rarely
 //     taken exact branch rescales when a half's probabilities could grow too
-//     large. The normaliser sums the same bf16 P the PV product uses.
+//     large. The normaliser sums the probabilities in float32, before they
+//     are rounded to bf16 for the PV product.
 //   * FP8 variant (press summary section 5: FP8 with per-token activation
 //     scales; single-stage walk, D = 128): queries and keys as E4M3 codes
 //     with E8M0 scales per 32 channels of a token, scores on the scaled FP8
@@ -316,18 +317,18 @@ struct Walk {
       b1[e] = (__bf16)p[8 + e];
     }
   }
-  // Sum of the 16 bf16 probabilities (two dot products with (1, 1) per pair
-  // of registers): the normaliser adds exactly the rounded values the PV
-  // MFMA multiplies.
-  static __device__ __forceinline__ float psum(const bf16x8& b0, const bf16x8& b1) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    float a = 0.0f, c = 0.0f;
+  // Sum of a lane's 16 float32 probabilities (a tree of adds), taken before
+  // they are rounded to bf16 for the PV product. Plain float adds rather than
+  // the bf16 dot instruction: on gfx950 a dot product waits for the matrix
+  // core while another wavefront's MFMAs run (3.5x slower beside them in an
+  // issue probe; float adds 1.4x).
+  static __device__ __forceinline__ float psum(const f32x16& p) {
+    float t[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{b0[2 * i], b0[2 * i + 1]}, one, a, false);
-      c = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{b1[2 * i], b1[2 * i + 1]}, one, c, false);
-    }
-    return a + c;
+    for (int i = 0; i < 8; ++i) t[i] = p[2 * i] + p[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+    return (t[0] + t[1]) + (t[2] + t[3]);
   }
   // The exact path for one half, taken when the fast path's probabilities
   // could be too large (or the walk has no reference yet): recompute the
@@ -434,11 +435,11 @@ struct Walk {
     for (int i = QSTEPS / 2; i < LI; ++i) issue_one<true>(nx, i);
     bf16x8 b0, b1;
     to_bf16(s0, b0, b1);
-    ps0 = psum(b0, b1);
+    ps0 = psum(s0);
     if (__builtin_amdgcn_ballot_w64(!(ps0 <= kFastLimit)) != 0) {
       exact_half(ks, 0, count, s0);
       to_bf16(s0, b0, b1);
-      ps0 = psum(b0, b1);
+      ps0 = psum(s0);
     }
     l_run += ps0;
     if (count < BN) mask_half(s1, 1, count);
@@ -462,11 +463,11 @@ struct Walk {
       LF_FENCE;
     }
     to_bf16(s1, b0, b1);
-    ps1 = psum(b0, b1);
+    ps1 = psum(s1);
     if (__builtin_amdgcn_ballot_w64(!(ps1 <= kFastLimit)) != 0) {
       exact_half(ks, 1, count, s1);
       to_bf16(s1, b0, b1);
-      ps1 = psum(b0, b1);
+      ps1 = psum(s1);
     }
     l_run += ps1;
     LF_FENCE;
@@ -561,11 +562,11 @@ struct Walk {
       LF_FENCE;
     }
     to_bf16(s0, b0, b1);
-    float ps0 = psum(b0, b1);
+    float ps0 = psum(s0);
     if (__builtin_amdgcn_ballot_w64(!(ps0 <= kFastLimit)) != 0) {
       exact_half(ks, 0, count, s0);
       to_bf16(s0, b0, b1);
-      ps0 = psum(b0, b1);
+      ps0 = psum(s0);
     }
     l_run += ps0;
     if (count < BN) mask_half(s1, 1, count);
@@ -613,11 +614,11 @@ struct Walk {
       LF_FENCE;
     }
     to_bf16(s0, b0, b1);
-    float ps0 = psum(b0, b1);
+    float ps0 = psum(s0);
     if (__builtin_amdgcn_ballot_w64(!(ps0 <= kFastLimit)) != 0) {
       exact_half_q8(ks, 0, count, s0);
       to_bf16(s0, b0, b1);
-      ps0 = psum(b0, b1);
+      ps0 = psum(s0);
     }
     l_run += ps0;
     if (count < BN) mask_half(s1, 1, count);
@@ -651,12 +652,12 @@ struct Walk {
 #pragma unroll
     for (int i = 2 * DB; i < LI; ++i) issue_one<false>(nk, i);
     to_bf16(s1, b0, b1);
-    float ps1 = psum(b0, b1);
+    float ps1 = psum(s1);
     if (__builtin_amdgcn_ballot_w64(!(ps1 <= kFastLimit)) != 0) {
       s1 = s1raw;
       exact_from_scores(s1);
       to_bf16(s1, b0, b1);
-      ps1 = psum(b0, b1);
+      ps1 = psum(s1);
     }
     l_run += ps1;
     LF_FENCE;
@@ -715,11 +716,11 @@ struct Walk {
     load_v(vs, 0, va);
     bf16x8 b0, b1;
     to_bf16(s0, b0, b1);
-    float ps0 = psum(b0, b1);
+    float ps0 = psum(s0);
     if (__builtin_amdgcn_ballot_w64(!(ps0 <= kFastLimit)) != 0) {
       exact_half_q8(ks, 0, count, s0);
       to_bf16(s0, b0, b1);
-      ps0 = psum(b0, b1);
+      ps0 = psum(s0);
     }
     l_run += ps0;
     if (count < BN) mask_half(s1, 1, count);
@@ -739,11 +740,11 @@ struct Walk {
       LF_FENCE;
     }
     to_bf16(s1, b0, b1);
-    float ps1 = psum(b0, b1);
+    float ps1 = psum(s1);
     if (__builtin_amdgcn_ballot_w64(!(ps1 <= kFastLimit)) != 0) {
       exact_half_q8(ks, 1, count, s1);
       to_bf16(s1, b0, b1);
-      ps1 = psum(b0, b1);
+      ps1 = psum(s1);
     }
     l_run += ps1;
     LF_FENCE;
