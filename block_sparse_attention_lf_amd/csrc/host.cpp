@@ -80,6 +80,12 @@ int64_t max_sel_of(const lf::KGeom& g, int32_t k_frames, int32_t k_blocks) {
 
 extern "C" {
 
+// Hash of the sources this library was built from (set by the build).
+#ifndef LF_BUILD_ID
+#define LF_BUILD_ID "unversioned"
+#endif
+const char* lf_build_id(void) { return LF_BUILD_ID; }
+
 const char* lf_status_str(lf_status s) {
   switch (s) {
     case LF_OK: return "LF_OK";

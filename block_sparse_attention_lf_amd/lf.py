@@ -32,7 +32,7 @@ STATUS = {0: "LF_OK", -1: "LF_ERR_NULL", -2: "LF_ERR_GEOM", -3: "LF_ERR_DTYPE", 
 # Every symbol include/lf.h declares.
 EXPORTS = ("lf_compress", "lf_max_sel", "lf_select", "lf_max_sel_1d", "lf_select_blocks", "lf_pool_keys", "lf_select_fused", "lf_block_sparse_attn",
            "lf_block_sparse_attn_fp8", "lf_block_sparse_attn_bwd", "lf_block_sparse_attn_bwd_noalloc",
-           "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error")
+           "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error", "lf_build_id")
 
 
 class LfError(RuntimeError):
@@ -64,6 +64,13 @@ _I32P = ctypes.POINTER(ctypes.c_int32)
 _F64P = ctypes.POINTER(ctypes.c_double)
 
 
+def expected_build_id() -> str:
+    """The id a library built from this tree's sources carries."""
+    from block_sparse_attention_lf_amd.build import source_hash
+
+    return source_hash()
+
+
 def lib() -> ctypes.CDLL:
     """Load liblf.so (raises if it is missing: there is no other implementation)."""
     global _lib
@@ -72,6 +79,12 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run `python -m block_sparse_attention_lf_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
+    L.lf_build_id.restype = ctypes.c_char_p
+    L.lf_build_id.argtypes = []
+    built, tree = L.lf_build_id().decode(), expected_build_id()
+    if built != tree:
+        raise RuntimeError(f"{LIB_PATH} was built from other sources (id {built}, tree {tree}); "
+                           "run `python -m block_sparse_attention_lf_amd.build`")
     G = ctypes.POINTER(lf_geom)
     sig = {
         "lf_compress": (ctypes.c_int, [G, _P, _P, _I32P, _P, _P, _P, _P]),
@@ -96,6 +109,7 @@ def lib() -> ctypes.CDLL:
         "lf_cache_frame_slots": (ctypes.c_int, [ctypes.c_int32] * 5 + [_I32P, _I32P, _I32P]),
         "lf_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "lf_last_error": (ctypes.c_char_p, []),
+        "lf_build_id": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

@@ -313,6 +313,9 @@ lf_status lf_cache_frame_slots(int32_t policy, int32_t cache_slots, int32_t n_si
 
 /* Human-readable status name; the detail of the last failure on this thread. */
 const char* lf_status_str(lf_status s);
+/* Hash of the sources (csrc/ and this header) the library was built from;
+ * the Python binding refuses a library whose id differs from its tree's. */
+const char* lf_build_id(void);
 const char* lf_last_error(void);
 
 #ifdef __cplusplus

@@ -234,3 +234,14 @@ def test_binding_limits_match_the_header():
     assert defs, "no LF_MAX_ limits found"
     for name, value in defs.items():
         assert getattr(lf, name) == value, name
+
+
+def test_library_carries_the_id_of_its_sources_and_a_stale_one_is_refused(monkeypatch):
+    """liblf.so embeds a hash of the sources it was built from; the binding refuses a library whose id
+    differs from the tree's (a stale build shipped with edited sources)."""
+    L = lf.lib()
+    assert L.lf_build_id().decode() == lf.expected_build_id()
+    monkeypatch.setattr(lf, "_lib", None)
+    monkeypatch.setattr(lf, "expected_build_id", lambda: "0" * 16)
+    with pytest.raises(RuntimeError, match="built from other sources"):
+        lf.lib()
