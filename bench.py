@@ -407,7 +407,7 @@ def main():
                    "hist_frames": w.hist_frames, "k_frames": w.k_frames, "k_blocks": w.k_blocks,
                    "sparsity": w.sparsity, "input_sets_rotated": N_SETS, "path": args.path,
                    "bytes_per_input_set": int(leg.set_bytes)},
-        "roofline": {"bound": "mfma", "kernel": "attn_group_kernel (lf_block_sparse_attn)",
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel (lf_block_sparse_attn)",
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": flops_mean, "avg_launch_ms": round(attn_ms, 4)},
@@ -502,7 +502,7 @@ def main():
                          "peak": round(fpeak, 1), "unit": "TFLOP/s", "frac": round(fach / fpeak, 4),
                          "frac_of_bf16_peak": round(fach / PEAK_BF16_TFLOPS, 4),
                          "speedup_vs_bf16_attention": round(attn_ms / fms, 3),
-                         "kernel": "attn_group_kernel Q8 (lf_block_sparse_attn_fp8)"}
+                         "kernel": "attn_kernel Q8 (lf_block_sparse_attn_fp8)"}
     if not args.headline_only:
         # The other workloads on the same clock: long history with a sink and the
         # wide-head case (one input set each beyond what the MALL holds), then
