@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the 480p chunk)")
+    ap.add_argument("--sets", type=int, default=N_SETS,
+                    help="input sets rotated over the steps (default 4, together larger than the MALL)")
     ap.add_argument("--path", choices=("step", "fused"), default="step",
                     help="step: compress + select + attention every step (every hot-path row); fused: keys pooled "
                          "once on commit, then fused query pooling + selection and attention per step")
@@ -386,7 +388,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     w = I.WORKLOADS[args.workload] if args.workload else I.WAN480P_CHUNK
-    leg = Leg(w, N_SETS, args.path)
+    leg = Leg(w, max(1, args.sets), args.path)
     g, scale, slots, bufs, stream = leg.g, leg.scale, leg.slots, leg.bufs, leg.stream
     host0 = leg.host0
     sets = leg.sets
@@ -405,7 +407,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "tokens_per_frame": w.tokens_per_frame, "block": w.block, "chunk_frames": w.chunk_frames,
                    "hist_frames": w.hist_frames, "k_frames": w.k_frames, "k_blocks": w.k_blocks,
-                   "sparsity": w.sparsity, "input_sets_rotated": N_SETS, "path": args.path,
+                   "sparsity": w.sparsity, "input_sets_rotated": len(leg.sets), "path": args.path,
                    "bytes_per_input_set": int(leg.set_bytes)},
         "roofline": {"bound": "mfma", "kernel": "attn_kernel (lf_block_sparse_attn)",
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
@@ -446,8 +448,8 @@ def main():
         dv = torch.empty(sets[0][1].shape, dtype=torch.float32, device="cuda")
 
         def bwd(i):
-            q, kc, vc = sets[i % N_SETS]
-            o, ls, do, sb, nsl = bw[i % N_SETS]
+            q, kc, vc = sets[i % len(sets)]
+            o, ls, do, sb, nsl = bw[i % len(sets)]
             lf.lf_block_sparse_attn_bwd(g, q, kc, vc, slots, sb, nsl, scale, o, ls, do, delta, dq, dk, dv, stream)
 
         for i in range(args.warmup):
@@ -482,8 +484,8 @@ def main():
         out8 = torch.empty_like(bufs.out)
 
         def fwd8(i):
-            q8, qs, k8, ks, sb, nsl = f8[i % N_SETS]
-            lf.lf_block_sparse_attn_fp8(g, q8, qs, k8, ks, sets[i % N_SETS][2], slots, sb, nsl, scale, out8, None,
+            q8, qs, k8, ks, sb, nsl = f8[i % len(sets)]
+            lf.lf_block_sparse_attn_fp8(g, q8, qs, k8, ks, sets[i % len(sets)][2], slots, sb, nsl, scale, out8, None,
                                         stream)
 
         for i in range(args.warmup):

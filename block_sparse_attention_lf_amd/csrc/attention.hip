@@ -127,10 +127,21 @@ struct Walk {
   static constexpr bool kSplitPitch = SPLIT_PITCH && ES == 2 && D == 128;
   static constexpr int KES = Q8 ? 1 : ES;                       // bytes per key element
   static constexpr int CPRK = D * KES / 16;                     // 16-byte chunks per key row
+  // bf16 rows of 256 bytes (D = 128) are stored unpadded with the 16-byte
+  // chunks of row r permuted: LDS chunk c' of row r holds chunk c' ^ sw(r),
+  // sw(r) = 4*(r%4) + (r/4)%4. Both read patterns are then free of bank
+  // conflicts: the K reads (16 consecutive rows, one chunk each: sw takes all
+  // 16 values) and the transposing V reads (4 consecutive rows from a
+  // multiple of 4, 4 consecutive chunks each: (4a + m) ^ (4k + q) takes 16
+  // values over rows k and chunks m). The DMA writes stay contiguous, no
+  // pad bytes are loaded, and a read address is a per-lane base XOR a
+  // constant.
+  static constexpr bool kSwzK = ES == 2 && D == 128 && !Q8;
+  static constexpr bool kSwzV = ES == 2 && D == 128;
   // (FP8 key rows: 16-byte pad, the two 16-byte reads per lane of a row
   // then fall in distinct bank groups)
-  static constexpr int RSK = D * KES + (Q8 ? 16 : (kSplitPitch ? 16 : 32));  // K row pitch in bytes
-  static constexpr int RSV = D * ES + (kSplitPitch ? 64 : 32);  // V row pitch in bytes
+  static constexpr int RSK = kSwzK ? 256 : D * KES + (Q8 ? 16 : (kSplitPitch ? 16 : 32));  // K row pitch in bytes
+  static constexpr int RSV = kSwzV ? 256 : D * ES + (kSplitPitch ? 64 : 32);  // V row pitch in bytes
   static constexpr int SPRK = RSK / 16, SPRV = RSV / 16;       // 16-byte slots per row (CPR data + pad)
   static constexpr int SLOTS_K = BN * SPRK, SLOTS_V = BN * SPRV;
   static constexpr int LIK = (SLOTS_K + NT - 1) / NT;          // load instructions per wavefront per K tile
@@ -197,7 +208,12 @@ struct Walk {
   // (lane l the l-th); this lane's slot holds chunk c of key row `row`, i.e.
   // byte offset row*D*ES + c*16 from the tile's first key.
   uint32_t doffk[LIK], doffv[LIV];
-  static __device__ __forceinline__ uint32_t slot_offset(int slot, int spr, int cpr, int row_bytes) {
+  static __device__ __forceinline__ int swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+  static __device__ __forceinline__ uint32_t slot_offset(int slot, int spr, int cpr, int row_bytes, bool swizzled) {
+    if (swizzled) {  // 16 slots per row, no pad: slot (row, c') holds chunk c' ^ sw(row)
+      const int row = slot >> 4;
+      return (uint32_t)(row * row_bytes + (((slot & 15) ^ swz(row)) * 16));
+    }
     const int row = min(slot / spr, BN - 1);
     int c = slot - (slot / spr) * spr;
     while (c >= cpr) c -= cpr;  // a pad slot re-reads a chunk its row already loads (same cache line)
@@ -205,9 +221,9 @@ struct Walk {
   }
   __device__ __forceinline__ void init_loads() {
 #pragma unroll
-    for (int i = 0; i < LIK; ++i) doffk[i] = slot_offset((i * NW + wv) * 64 + lane, SPRK, CPRK, D * KES);
+    for (int i = 0; i < LIK; ++i) doffk[i] = slot_offset((i * NW + wv) * 64 + lane, SPRK, CPRK, D * KES, kSwzK);
 #pragma unroll
-    for (int i = 0; i < LIV; ++i) doffv[i] = slot_offset((i * NW + wv) * 64 + lane, SPRV, CPR, D * ES);
+    for (int i = 0; i < LIV; ++i) doffv[i] = slot_offset((i * NW + wv) * 64 + lane, SPRV, CPR, D * ES, kSwzV);
   }
 
   // The next tile's loads, described at the top of an iteration and issued
@@ -283,12 +299,19 @@ struct Walk {
   // ---- bf16 tile math ----------------------------------------------------
   // K fragments of key half kh (keys 32kh .. 32kh+31) for S^T = K Q^T.
   __device__ __forceinline__ void load_k(const char* ks, int kh, frag (&kf)[QSTEPS]) const {
-    const char* krow = ks + (kh * 32 + l32) * RSK + h * 16;
 #pragma unroll
-    for (int t = 0; t < QSTEPS; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(krow + t * 32);
+    for (int t = 0; t < QSTEPS; ++t) kf[t] = load_k1(ks, kh, t);
   }
   __device__ __forceinline__ frag load_k1(const char* ks, int kh, int t) const {
-    return *reinterpret_cast<const bf16x8*>(ks + (kh * 32 + l32) * RSK + h * 16 + t * 32);
+    if constexpr (kSwzK) {
+      // chunk 2t+h of row r sits at chunk (2t+h) ^ sw(r): with sw = 2*xh + x0,
+      // byte offset 32*(t ^ xh) + 16*(h ^ x0), i.e. a per-lane base XOR 32t
+      const int x = swz(l32);
+      const uint32_t base = (uint32_t)(l32 * 256 + 32 * (x >> 1) + 16 * (h ^ (x & 1)));
+      return *reinterpret_cast<const bf16x8*>(ks + kh * 32 * 256 + (base ^ (uint32_t)(32 * t)));
+    } else {
+      return *reinterpret_cast<const bf16x8*>(ks + (kh * 32 + l32) * RSK + h * 16 + t * 32);
+    }
   }
   // V^T fragments (A operand) of the 16-key step ps for every 32-column block.
   __device__ __forceinline__ void load_v(const char* vs, int ps, bf16x8 (&a)[DB]) const {
@@ -297,12 +320,25 @@ struct Walk {
   }
   __device__ __forceinline__ bf16x8 load_v1(const char* vs, int ps, int db) const {
     const int s16 = lane & 15;
-    // lane's key inside an 8-key group and its first column inside a 32-column block
-    const char* vbase = vs + (4 * h + (s16 >> 2)) * RSV + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
     i16x4 part[2];
+    if constexpr (kSwzV) {
+      // row 4h + s16/4 + 16ps + 8j (sw = 4*(s16/4) + h + 2j), chunk
+      // 4db + cb with cb = 2*((lane/16)&1) + (s16&3)/2, half s16&1: the chunk
+      // bits are (4*(s16/4) + (cb ^ h)) ^ (4db + 2j), a per-lane base XOR a
+      // constant; the row offset 16ps + 8j is added after.
+      const int cb = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+      const uint32_t base = (uint32_t)((4 * h + (s16 >> 2)) * 256 + 16 * (4 * (s16 >> 2) + (cb ^ h)) + 8 * (s16 & 1));
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vbase + (16 * ps + 8 * j) * RSV + 64 * db));
+      for (int j = 0; j < 2; ++j)
+        part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            LDS_PTR(i16x4, vs + (16 * ps + 8 * j) * 256 + (base ^ (uint32_t)(16 * (4 * db + 2 * j)))));
+    } else {
+      // lane's key inside an 8-key group and its first column inside a 32-column block
+      const char* vbase = vs + (4 * h + (s16 >> 2)) * RSV + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vbase + (16 * ps + 8 * j) * RSV + 64 * db));
+    }
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
   }
   __device__ __forceinline__ void mask_half(f32x16& s, int kh, int count) const {
