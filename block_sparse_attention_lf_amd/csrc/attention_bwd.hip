@@ -290,12 +290,23 @@ __global__ __launch_bounds__(64 * WPQ, (KT == 32 && WPQ >= 2 ? 2 : 1)) void bwd_
   for (int db = 0; db < S::DB; ++db) store_acc_t(dst, acc[db], db, h, scale);
 }
 
+// Element e of a packed bf16x8 as a float, from the 32-bit word holding it.
+__device__ inline float bf16_word_elt(const bf16x8& v, int e) {
+  const uint4 w = __builtin_bit_cast(uint4, v);
+  const uint32_t x = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
+  return __builtin_bit_cast(float, (e & 1) ? (x & 0xffff0000u) : (x << 16));
+}
+
 // One query block against this wavefront's 32 keys (K^T, V^T in registers):
 // per 32 query rows, S = Q K^T and P; dV^T += dO^T P, or dP = dO V^T,
-// dS = P (dP - D) and dK^T += Q^T dS. ls holds lse*log2(e) per row (+inf on
-// missing rows, so their P is 0), dd the row's D.
+// dS = P (dP - D) and dK^T += Q^T dS. The row terms enter as the starting
+// values of the accumulators, so no per-row value stays live across the
+// MFMA chains: ls holds -lse/scale per row (-inf on missing rows, so their P
+// is 0), and the score accumulator starts there, giving
+// P = 2^(scale*log2(e) * (s - lse/scale)); nd holds -D per row, and the dP
+// accumulator starts there, giving dP - D.
 template <int D>  // adv: dV^T accumulators, adk: dK^T accumulators
-__device__ inline void dkv_block_math(const char* qs, const char* gs, const float* ls, const float* dd, int nrows,
+__device__ inline void dkv_block_math(const char* qs, const char* gs, const float* ls, const float* nd, int nrows,
                                       const bf16x8* kf, const bf16x8* vf, f32x16* adv, f32x16* adk, float c2,
                                       bool kok, int lane) {
   using S = BwdShape<D>;
@@ -304,37 +315,38 @@ __device__ inline void dkv_block_math(const char* qs, const char* gs, const floa
   for (int qh = 0; qh < halves; ++qh) {
     f32x16 s;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+    for (int r = 0; r < 16; ++r) s[r] = ls[32 * qh + acc_row(r, h)];
 #pragma unroll
     for (int st = 0; st < S::QSTEPS; ++st)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qs, 32 * qh, st, l32, h), kf[st], s, 0, 0, 0);
-    float p[16];
+    // P, rounded to bf16 once: the dV product and dS both use these values.
+    // They stay packed (eight registers) across the dP product: the empty asm
+    // makes the packed words opaque, so the compiler cannot keep the sixteen
+    // unpacked values alive instead, and dS unpacks them from the words.
+    bf16x8 p0, p1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      p[r] = kok ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -ls[32 * qh + acc_row(r, h)])) : 0.0f;
-    {  // dV^T += dO^T P
-      bf16x8 b0, b1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (r < 8) b0[r] = (__bf16)p[r]; else b1[r - 8] = (__bf16)p[r];
-      }
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db) {
-        adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh, db, lane), b0, adv[db], 0, 0, 0);
-        adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh + 1, db, lane), b1, adv[db], 0, 0, 0);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const __bf16 pr = (__bf16)(kok ? __builtin_amdgcn_exp2f(s[r] * c2) : 0.0f);
+      if (r < 8) p0[r] = pr; else p1[r - 8] = pr;
     }
-    {  // dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
+    asm volatile("" : "+v"(p0), "+v"(p1));
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) {  // dV^T += dO^T P
+      adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh, db, lane), p0, adv[db], 0, 0, 0);
+      adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh + 1, db, lane), p1, adv[db], 0, 0, 0);
+    }
+    {  // dP - D = dO V^T - D, dS = P (dP - D), dK^T += Q^T dS
       f32x16 dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = 0.0f;
+      for (int r = 0; r < 16; ++r) dp[r] = nd[32 * qh + acc_row(r, h)];
 #pragma unroll
       for (int st = 0; st < S::QSTEPS; ++st)
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(gs, 32 * qh, st, l32, h), vf[st], dp, 0, 0, 0);
       bf16x8 b0, b1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const __bf16 d = (__bf16)(p[r] * (dp[r] - dd[32 * qh + acc_row(r, h)]));
+        const float pr = r < 8 ? bf16_word_elt(p0, r) : bf16_word_elt(p1, r - 8);
+        const __bf16 d = (__bf16)(pr * dp[r]);
         if (r < 8) b0[r] = d; else b1[r - 8] = d;
       }
 #pragma unroll
@@ -400,7 +412,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
   const int64_t krow0 = (bh * g.S + g.slot[f]) * (int64_t)g.T + start;
   const int key = 32 * wv + l32;
   const bool kok = key < count;
-  const float c2 = scale * kLog2e;
+  const float c2 = scale * kLog2e, inv_scale = 1.0f / scale;
 
   bf16x8 kf[S::QSTEPS], vf[S::QSTEPS];
 #pragma unroll
@@ -464,9 +476,11 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
     if (nq == 0) continue;
     // Steps of at most MAXQ query rows: a query block of more rows is taken
     // in several steps. Stage the first step; then per step: wait, barrier,
-    // start the next step's loads into the other stage, compute, and write
-    // the next step's lse / delta rows (loaded before its tiles, so already
-    // here).
+    // start the next step's lse / delta row loads (into registers) and its
+    // tile loads into the other stage, compute, and write those rows to LDS.
+    // The row loads go out after the barrier, ahead of the tiles, so the
+    // computation covers their latency and the wait before the write leaves
+    // the tile loads in flight.
     // Rows [r0, r0 + rows) of step (ii, hh): part hh of query block qlist[ii],
     // which has qrows rows in all.
     auto locate = [&](int ii, int hh, int64_t& r0, int& rows, int& qrows) {
@@ -480,8 +494,8 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
     int64_t row0 = 0;
     locate(0, 0, row0, nrows, qrows);
     if (tid < MAXQ) {
-      ls0[tid] = tid < nrows ? lse[row0 + tid] * kLog2e : INFINITY;  // +inf: P = 0 on missing rows
-      ds0[tid] = tid < nrows ? delta[row0 + tid] : 0.0f;
+      ls0[tid] = tid < nrows ? -lse[row0 + tid] * inv_scale : -INFINITY;  // -inf: P = 0 on missing rows
+      ds0[tid] = tid < nrows ? -delta[row0 + tid] : 0.0f;
     }
     dma.issue(qs0, q + row0 * D, nrows, tid);
     dma.issue(gs0, dout + row0 * D, nrows, tid);
@@ -498,24 +512,22 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
     } else {                                                                                \
       more = false;                                                                         \
     }                                                                                       \
-    float nl = 0.0f, nd = 0.0f;                                                             \
-    if (more) {                                                                             \
-      locate(i, hq, row0, nrows, qrows);                                                    \
-      if (tid < nrows) {                                                                    \
-        nl = lse[row0 + tid];                                                               \
-        nd = delta[row0 + tid];                                           \
-      }                                                                                     \
-    }                                                                                       \
+    if (more) locate(i, hq, row0, nrows, qrows);                                            \
     __builtin_amdgcn_s_waitcnt(kWaitVm0);                                                   \
     __syncthreads();                                                                        \
+    float nl = 0.0f, nd = 0.0f;                                                             \
     if (more) {                                                                             \
+      if (tid < nrows) {                                                                    \
+        nl = lse[row0 + tid];                                                               \
+        nd = delta[row0 + tid];                                                             \
+      }                                                                                     \
       dma.issue(QB, q + row0 * D, nrows, tid);                                              \
       dma.issue(GB, dout + row0 * D, nrows, tid);                                           \
     }                                                                                       \
     dkv_block_math<D>(QA, GA, LA, DA, cur_rows, kf, vf, adv, adk, c2, kok, lane);           \
     if (more && tid < MAXQ) {                                                               \
-      LB[tid] = tid < nrows ? nl * kLog2e : INFINITY;                                       \
-      DB_[tid] = nd;                                                      \
+      LB[tid] = tid < nrows ? -nl * inv_scale : -INFINITY;                                  \
+      DB_[tid] = -nd;                                                                       \
     }                                                                                       \
     have = more;                                                                            \
   }
