@@ -290,6 +290,23 @@ __global__ __launch_bounds__(64 * WPQ, (KT == 32 && WPQ >= 2 ? 2 : 1)) void bwd_
   for (int db = 0; db < S::DB; ++db) store_acc_t(dst, acc[db], db, h, scale);
 }
 
+// Element i of rows [row0, row0 + n) of a float array (0 past n), read
+// through a buffer resource: the base stays in scalar registers and the lane
+// holds a 32-bit offset, not a 64-bit address.
+__device__ inline float row_value(const float* base, int64_t row0, int n, int i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(uniform_ptr(base + row0)), (short)0, n * 4, kRawBufferFlags);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0));
+#else
+  (void)base;
+  (void)row0;
+  (void)n;
+  (void)i;
+  return 0.0f;
+#endif
+}
+
 // Element e of a packed bf16x8 as a float, from the 32-bit word holding it.
 __device__ inline float bf16_word_elt(const bf16x8& v, int e) {
   const uint4 w = __builtin_bit_cast(uint4, v);
@@ -304,55 +321,97 @@ __device__ inline float bf16_word_elt(const bf16x8& v, int e) {
 // MFMA chains: ls holds -lse/scale per row (-inf on missing rows, so their P
 // is 0), and the score accumulator starts there, giving
 // P = 2^(scale*log2(e) * (s - lse/scale)); nd holds -D per row, and the dP
-// accumulator starts there, giving dP - D.
-template <int D>  // adv: dV^T accumulators, adk: dK^T accumulators
+// accumulator starts there, giving dP - D. IL: the S and dP chains (and the
+// dV and dK ones) interleaved, which needs sixteen more registers; the
+// history pass, which holds more state, runs them one after the other.
+template <int D, bool IL>  // adv: dV^T accumulators, adk: dK^T accumulators
 __device__ inline void dkv_block_math(const char* qs, const char* gs, const float* ls, const float* nd, int nrows,
                                       const bf16x8* kf, const bf16x8* vf, f32x16* adv, f32x16* adk, float c2,
                                       bool kok, int lane) {
   using S = BwdShape<D>;
   const int l32 = lane & 31, h = lane >> 5;
   const int halves = (nrows + 31) / 32;
-  for (int qh = 0; qh < halves; ++qh) {
-    f32x16 s;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = ls[32 * qh + acc_row(r, h)];
-#pragma unroll
-    for (int st = 0; st < S::QSTEPS; ++st)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qs, 32 * qh, st, l32, h), kf[st], s, 0, 0, 0);
-    // P, rounded to bf16 once: the dV product and dS both use these values.
-    // They stay packed (eight registers) across the dP product: the empty asm
-    // makes the packed words opaque, so the compiler cannot keep the sixteen
-    // unpacked values alive instead, and dS unpacks them from the words.
-    bf16x8 p0, p1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const __bf16 pr = (__bf16)(kok ? __builtin_amdgcn_exp2f(s[r] * c2) : 0.0f);
-      if (r < 8) p0[r] = pr; else p1[r - 8] = pr;
-    }
-    asm volatile("" : "+v"(p0), "+v"(p1));
-#pragma unroll
-    for (int db = 0; db < S::DB; ++db) {  // dV^T += dO^T P
-      adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh, db, lane), p0, adv[db], 0, 0, 0);
-      adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh + 1, db, lane), p1, adv[db], 0, 0, 0);
-    }
-    {  // dP - D = dO V^T - D, dS = P (dP - D), dK^T += Q^T dS
-      f32x16 dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = nd[32 * qh + acc_row(r, h)];
-#pragma unroll
-      for (int st = 0; st < S::QSTEPS; ++st)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(gs, 32 * qh, st, l32, h), vf[st], dp, 0, 0, 0);
-      bf16x8 b0, b1;
+  if constexpr (IL) {
+    for (int qh = 0; qh < halves; ++qh) {
+      // S - lse/scale and dP - D as two interleaved MFMA chains (each one's
+      // fragment reads overlap the other's products).
+      f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = r < 8 ? bf16_word_elt(p0, r) : bf16_word_elt(p1, r - 8);
-        const __bf16 d = (__bf16)(pr * dp[r]);
-        if (r < 8) b0[r] = d; else b1[r - 8] = d;
+        s[r] = ls[32 * qh + acc_row(r, h)];
+        dp[r] = nd[32 * qh + acc_row(r, h)];
       }
 #pragma unroll
-      for (int db = 0; db < S::DB; ++db) {
+      for (int st = 0; st < S::QSTEPS; ++st) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qs, 32 * qh, st, l32, h), kf[st], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(gs, 32 * qh, st, l32, h), vf[st], dp, 0, 0, 0);
+      }
+      // P and dS = P (dP - D), rounded to bf16 (dS from the rounded P, the
+      // values the dV product uses).
+      bf16x8 p0, p1, b0, b1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const __bf16 pr = (__bf16)(kok ? __builtin_amdgcn_exp2f(s[r] * c2) : 0.0f);
+        const __bf16 d = (__bf16)((float)pr * dp[r]);
+        if (r < 8) {
+          p0[r] = pr;
+          b0[r] = d;
+        } else {
+          p1[r - 8] = pr;
+          b1[r - 8] = d;
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) {  // dV^T += dO^T P, dK^T += Q^T dS
+        adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh, db, lane), p0, adv[db], 0, 0, 0);
         adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qs, 2 * qh, db, lane), b0, adk[db], 0, 0, 0);
+        adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh + 1, db, lane), p1, adv[db], 0, 0, 0);
         adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qs, 2 * qh + 1, db, lane), b1, adk[db], 0, 0, 0);
+      }
+    }
+  } else {
+    for (int qh = 0; qh < halves; ++qh) {
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = ls[32 * qh + acc_row(r, h)];
+#pragma unroll
+      for (int st = 0; st < S::QSTEPS; ++st)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qs, 32 * qh, st, l32, h), kf[st], s, 0, 0, 0);
+      // P, rounded to bf16 once: the dV product and dS both use these values.
+      // They stay packed (eight registers) across the dP product: the empty asm
+      // makes the packed words opaque, so the compiler cannot keep the sixteen
+      // unpacked values alive instead, and dS unpacks them from the words.
+      bf16x8 p0, p1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const __bf16 pr = (__bf16)(kok ? __builtin_amdgcn_exp2f(s[r] * c2) : 0.0f);
+        if (r < 8) p0[r] = pr; else p1[r - 8] = pr;
+      }
+      asm volatile("" : "+v"(p0), "+v"(p1));
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) {  // dV^T += dO^T P
+        adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh, db, lane), p0, adv[db], 0, 0, 0);
+        adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(gs, 2 * qh + 1, db, lane), p1, adv[db], 0, 0, 0);
+      }
+      {  // dP - D = dO V^T - D, dS = P (dP - D), dK^T += Q^T dS
+        f32x16 dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = nd[32 * qh + acc_row(r, h)];
+#pragma unroll
+        for (int st = 0; st < S::QSTEPS; ++st)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(gs, 32 * qh, st, l32, h), vf[st], dp, 0, 0, 0);
+        bf16x8 b0, b1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = r < 8 ? bf16_word_elt(p0, r) : bf16_word_elt(p1, r - 8);
+          const __bf16 d = (__bf16)(pr * dp[r]);
+          if (r < 8) b0[r] = d; else b1[r - 8] = d;
+        }
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db) {
+          adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qs, 2 * qh, db, lane), b0, adk[db], 0, 0, 0);
+          adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qs, 2 * qh + 1, db, lane), b1, adk[db], 0, 0, 0);
+        }
       }
     }
   }
@@ -494,8 +553,8 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
     int64_t row0 = 0;
     locate(0, 0, row0, nrows, qrows);
     if (tid < MAXQ) {
-      ls0[tid] = tid < nrows ? -lse[row0 + tid] * inv_scale : -INFINITY;  // -inf: P = 0 on missing rows
-      ds0[tid] = tid < nrows ? -delta[row0 + tid] : 0.0f;
+      ls0[tid] = tid < nrows ? -row_value(lse, row0, nrows, tid) * inv_scale : -INFINITY;  // -inf: P = 0 on missing rows
+      ds0[tid] = -row_value(delta, row0, nrows, tid);
     }
     dma.issue(qs0, q + row0 * D, nrows, tid);
     dma.issue(gs0, dout + row0 * D, nrows, tid);
@@ -517,14 +576,14 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
     __syncthreads();                                                                        \
     float nl = 0.0f, nd = 0.0f;                                                             \
     if (more) {                                                                             \
-      if (tid < nrows) {                                                                    \
-        nl = lse[row0 + tid];                                                               \
-        nd = delta[row0 + tid];                                                             \
+      if (tid < MAXQ) {                                                                     \
+        nl = row_value(lse, row0, nrows, tid);                                              \
+        nd = row_value(delta, row0, nrows, tid);                                            \
       }                                                                                     \
       dma.issue(QB, q + row0 * D, nrows, tid);                                              \
       dma.issue(GB, dout + row0 * D, nrows, tid);                                           \
     }                                                                                       \
-    dkv_block_math<D>(QA, GA, LA, DA, cur_rows, kf, vf, adv, adk, c2, kok, lane);           \
+    dkv_block_math<D, CUR>(QA, GA, LA, DA, cur_rows, kf, vf, adv, adk, c2, kok, lane);           \
     if (more && tid < MAXQ) {                                                               \
       LB[tid] = tid < nrows ? -nl * inv_scale : -INFINITY;                                  \
       DB_[tid] = -nd;                                                                       \
