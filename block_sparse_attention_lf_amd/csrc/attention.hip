@@ -208,7 +208,7 @@ struct Walk {
   // (lane l the l-th); this lane's slot holds chunk c of key row `row`, i.e.
   // byte offset row*D*ES + c*16 from the tile's first key.
   uint32_t doffk[LIK], doffv[LIV];
-  static __device__ __forceinline__ int swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+  static __device__ __forceinline__ int swz(int row) { return lds_swizzle(row); }
   static __device__ __forceinline__ uint32_t slot_offset(int slot, int spr, int cpr, int row_bytes, bool swizzled) {
     if (swizzled) {  // 16 slots per row, no pad: slot (row, c') holds chunk c' ^ sw(row)
       const int row = slot >> 4;

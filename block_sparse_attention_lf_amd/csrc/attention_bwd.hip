@@ -35,7 +35,10 @@ namespace {
 
 template <int D>
 struct BwdShape {
-  static constexpr int RS = D * 2 + 32;  // LDS row pitch (bytes): bf16 row + 32-byte pad
+  // LDS rows: at d = 128, 256 bytes with 16-byte chunks XOR-swizzled per row
+  // (lds_swizzle); otherwise the bf16 row plus a 32-byte pad.
+  static constexpr bool SWZ = D == 128;
+  static constexpr int RS = SWZ ? 256 : D * 2 + 32;  // LDS row pitch (bytes)
   static constexpr int CPR = D * 2 / 16;  // 16-byte chunks per row
   static constexpr int QSTEPS = D / 16;   // MFMA reduction steps over d
   static constexpr int DB = D / 32;       // 32-column blocks of d
@@ -43,9 +46,10 @@ struct BwdShape {
 
 // Direct HBM -> LDS loads of a tile of ROWS rows (buffer loads that write
 // LDS, 16 bytes per lane, no registers). Load instruction i of wavefront w
-// fills 64 consecutive 16-byte LDS slots; slot s holds chunk s mod SPR of
-// row s / SPR, and the pad slots of a row re-read a chunk of the same row
-// (same cache line). The buffer resource spans the tile's `count` valid rows,
+// fills 64 consecutive 16-byte LDS slots. Swizzled rows: slot s holds chunk
+// (s mod 16) ^ lds_swizzle(row) of row s / 16. Padded rows: slot s holds
+// chunk s mod SPR of row s / SPR, and the pad slots of a row re-read a chunk
+// of the same row (same cache line). The buffer resource spans the tile's `count` valid rows,
 // so rows past it come back as zeros and no load leaves the matrix.
 template <int D, int ROWS, int NT>
 struct TileDma {
@@ -58,10 +62,15 @@ struct TileDma {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int slot = (i * (NT / 64) + wv) * 64 + lane;
-      const int row = min(slot / SPR, ROWS - 1);
-      int c = slot - (slot / SPR) * SPR;
-      while (c >= CPR) c -= CPR;
-      off[i] = (uint32_t)(row * D * 2 + c * 16);
+      if constexpr (BwdShape<D>::SWZ) {  // slot (row, c') holds chunk c' ^ lds_swizzle(row)
+        const int row = slot >> 4;
+        off[i] = (uint32_t)(row * D * 2 + ((slot & 15) ^ lds_swizzle(row)) * 16);
+      } else {
+        const int row = min(slot / SPR, ROWS - 1);
+        int c = slot - (slot / SPR) * SPR;
+        while (c >= CPR) c -= CPR;
+        off[i] = (uint32_t)(row * D * 2 + c * 16);
+      }
     }
   }
   __device__ inline void issue(char* lds, const __bf16* src, int count, int tid) const {
@@ -85,10 +94,19 @@ struct TileDma {
 };
 
 // MFMA operand fragments (lane l, l32 = l % 32, h = l / 32):
-// rows r0 + l32 of an LDS tile, d = 16t + 8h .. +7 (A operand, rows = M).
+// rows r0 + l32 of an LDS tile, d = 16t + 8h .. +7 (A operand, rows = M;
+// r0 a multiple of 32).
 template <int D>
 __device__ inline bf16x8 row_frag(const char* tile, int r0, int t, int l32, int h) {
-  return *reinterpret_cast<const bf16x8*>(tile + (r0 + l32) * BwdShape<D>::RS + (16 * t + 8 * h) * 2);
+  if constexpr (BwdShape<D>::SWZ) {
+    // chunk 2t+h of row r sits at (2t+h) ^ sw(r); with sw = 2*xh + x0 that is
+    // byte 32*(t ^ xh) + 16*(h ^ x0): a per-lane base XOR 32t
+    const int x = lds_swizzle(l32);
+    const uint32_t base = (uint32_t)(l32 * 256 + 32 * (x >> 1) + 16 * (h ^ (x & 1)));
+    return *reinterpret_cast<const bf16x8*>(tile + r0 * 256 + (base ^ (uint32_t)(32 * t)));
+  } else {
+    return *reinterpret_cast<const bf16x8*>(tile + (r0 + l32) * BwdShape<D>::RS + (16 * t + 8 * h) * 2);
+  }
 }
 // The transposed fragment of 16 rows (step ps) and 32 columns (block db):
 // A[d][row] with the rows in the order a 32x32 accumulator holds them, so
@@ -97,11 +115,23 @@ template <int D>
 __device__ inline bf16x8 tr_frag(const char* tile, int ps, int db, int lane) {
   constexpr int RS = BwdShape<D>::RS;
   const int s16 = lane & 15, h = lane >> 5;
-  const char* base = tile + (4 * h + (s16 >> 2)) * RS + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
   i16x4 part[2];
+  if constexpr (BwdShape<D>::SWZ) {
+    // row 4h + s16/4 + 16ps + 8j (sw = 4*(s16/4) + h + 2j), chunk 4db + cb
+    // with cb = 2*((lane/16)&1) + (s16&3)/2, half s16&1: the chunk bits are
+    // (4*(s16/4) + (cb ^ h)) ^ (4db + 2j), a per-lane base XOR a constant.
+    const int cb = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+    const uint32_t base = (uint32_t)((4 * h + (s16 >> 2)) * 256 + 16 * (4 * (s16 >> 2) + (cb ^ h)) + 8 * (s16 & 1));
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + (16 * ps + 8 * j) * RS + 64 * db));
+    for (int j = 0; j < 2; ++j)
+      part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          LDS_PTR(i16x4, tile + (16 * ps + 8 * j) * 256 + (base ^ (uint32_t)(16 * (4 * db + 2 * j)))));
+  } else {
+    const char* base = tile + (4 * h + (s16 >> 2)) * RS + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + (16 * ps + 8 * j) * RS + 64 * db));
+  }
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 // This lane's own row of a global matrix, d = 16t + 8h .. +7 (B operand,
@@ -324,14 +354,25 @@ __device__ inline float bf16_word_elt(const bf16x8& v, int e) {
 // accumulator starts there, giving dP - D. IL: the S and dP chains (and the
 // dV and dK ones) interleaved, which needs sixteen more registers; the
 // history pass, which holds more state, runs them one after the other.
-template <int D, bool IL>  // adv: dV^T accumulators, adk: dK^T accumulators
+//
+// issue_next() starts the next step's tile loads into the other stage. The
+// interleaved form calls it first; the other after the first score chain,
+// so that the K fragments that chain reads, if the compiler has spilled
+// them, are reloaded before the tile loads are in flight (a reload issued
+// after them would wait for them too).
+template <int D, bool IL, typename Issue>  // adv: dV^T accumulators, adk: dK^T accumulators
 __device__ inline void dkv_block_math(const char* qs, const char* gs, const float* ls, const float* nd, int nrows,
                                       const bf16x8* kf, const bf16x8* vf, f32x16* adv, f32x16* adk, float c2,
-                                      bool kok, int lane) {
+                                      bool kok, int lane, const Issue& issue_next) {
   using S = BwdShape<D>;
+  // The lane index is made opaque here, so the fragment addresses derived
+  // from it (one XOR per swizzled read) are recomputed at each step instead
+  // of being hoisted out of the walk and held in registers across it.
+  asm volatile("" : "+v"(lane));
   const int l32 = lane & 31, h = lane >> 5;
   const int halves = (nrows + 31) / 32;
   if constexpr (IL) {
+    issue_next();
     for (int qh = 0; qh < halves; ++qh) {
       // S - lse/scale and dP - D as two interleaved MFMA chains (each one's
       // fragment reads overlap the other's products).
@@ -370,6 +411,7 @@ __device__ inline void dkv_block_math(const char* qs, const char* gs, const floa
       }
     }
   } else {
+    if (halves == 0) issue_next();
     for (int qh = 0; qh < halves; ++qh) {
       f32x16 s;
 #pragma unroll
@@ -377,6 +419,7 @@ __device__ inline void dkv_block_math(const char* qs, const char* gs, const floa
 #pragma unroll
       for (int st = 0; st < S::QSTEPS; ++st)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qs, 32 * qh, st, l32, h), kf[st], s, 0, 0, 0);
+      if (qh == 0) issue_next();
       // P, rounded to bf16 once: the dV product and dS both use these values.
       // They stay packed (eight registers) across the dP product: the empty asm
       // makes the packed words opaque, so the compiler cannot keep the sixteen
@@ -580,10 +623,14 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
         nl = row_value(lse, row0, nrows, tid);                                              \
         nd = row_value(delta, row0, nrows, tid);                                            \
       }                                                                                     \
-      dma.issue(QB, q + row0 * D, nrows, tid);                                              \
-      dma.issue(GB, dout + row0 * D, nrows, tid);                                           \
     }                                                                                       \
-    dkv_block_math<D, CUR>(QA, GA, LA, DA, cur_rows, kf, vf, adv, adk, c2, kok, lane);           \
+    const auto issue_next = [&]() {                                                         \
+      if (more) {                                                                           \
+        dma.issue(QB, q + row0 * D, nrows, tid);                                            \
+        dma.issue(GB, dout + row0 * D, nrows, tid);                                         \
+      }                                                                                     \
+    };                                                                                      \
+    dkv_block_math<D, CUR>(QA, GA, LA, DA, cur_rows, kf, vf, adv, adk, c2, kok, lane, issue_next); \
     if (more && tid < MAXQ) {                                                               \
       LB[tid] = tid < nrows ? -nl * inv_scale : -INFINITY;                                  \
       DB_[tid] = -nd;                                                                       \

@@ -19,6 +19,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 // output: 8*(r/4) + 4*h + r%4 (the column is the lane index mod 32).
 __device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// LDS layout of 256-byte bf16 rows (d = 128) without padding: the 16-byte
+// chunk c of row r is stored at chunk position c ^ lds_swizzle(r). Reads of
+// 32 rows at one chunk (MFMA operand rows) and the transposing reads of 8
+// rows at 16 consecutive columns then spread over all banks.
+__device__ inline int lds_swizzle(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 only.
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
