@@ -90,12 +90,21 @@ def compress_bytes(w) -> float:
     return float(read + write)
 
 
-def file_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def sources_hash(paths) -> str:
+    """First 16 hex digits of the sha256 over the files' bytes, in the given order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_src: str, workload: str):
+# The attention kernel's sources: its own file and the headers it includes.
+ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_lf_amd", "csrc", f)
+                for f in ("attention.hip", "mfma.h", "lf_internal.h")]
+
+
+def traffic_from_profiles(workload: str):
     """HBM bytes per attention launch from committed rocprofv3 counter runs, if they match this kernel."""
     p = os.path.join(ROOT, "profiles", "attention_traffic.json")
     if not os.path.exists(p):
@@ -104,7 +113,7 @@ def traffic_from_profiles(kernel_src: str, workload: str):
         rec = json.load(open(p))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != file_hash(kernel_src) or rec.get("workload") != workload:
+    if rec.get("kernel_sources_sha256_16") != sources_hash(ATTN_SOURCES) or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -248,6 +257,12 @@ class Leg:
         if path == "fused":
             self._pool_on_commit()
 
+    def use_path(self, path: str):
+        """Switch the steps to the other path on the same input sets (pooling on commit when first needed)."""
+        self.path = path
+        if path == "fused" and not self.pooled:
+            self._pool_on_commit()
+
     def host_side(self):
         # a0: slot table of the cache for this chunk; a6: chunk budget (single call: its own sparsity)
         w, lf = self.w, self.lf
@@ -358,6 +373,23 @@ class Leg:
         return r
 
 
+def path_comparison(leg: "Leg", r: dict, steps: int, warmup: int) -> dict:
+    """The step path and the pool-on-commit path on the same input sets, one after the other in this process:
+    ms per step and stage times of each (r: the timing already taken on the leg's current path)."""
+    first = leg.path
+    other = "fused" if first == "step" else "step"
+    leg.use_path(other)
+    ro = leg.time(steps, warmup)
+    leg.use_path(first)
+    res = {first: r, other: ro}
+    out = {p: {"ms_per_step": round(x["ms_per_step"], 4), "stages_ms": {k: round(v, 4) for k, v in x["stages_ms"].items()}}
+           for p, x in res.items()}
+    out["fused"]["ms_per_commit"] = round(leg.commit_ms, 4)
+    out["fused"]["frames_per_commit"] = leg.w.chunk_frames
+    out["fused_over_step"] = round(res["fused"]["ms_per_step"] / res["step"]["ms_per_step"], 4)
+    return out
+
+
 def config_summary(leg: "Leg", r: dict, steps: int) -> dict:
     """Per-workload figures on the bench's own clock (the extra configurations)."""
     out = {"steps": steps, "input_sets_rotated": len(leg.sets), "ms_per_step": round(r["ms_per_step"], 4),
@@ -397,8 +429,7 @@ def main():
     ms_step, attn_ms, flops_mean, attn_tflops, peak = r["ms_per_step"], r["attn_ms"], r["flops"], r["attn_tflops"], \
         r["peak"]
     value = r["value"]
-    src = os.path.join(ROOT, "block_sparse_attention_lf_amd", "csrc", "attention.hip")
-    traffic = traffic_from_profiles(src, w.name)
+    traffic = traffic_from_profiles(w.name)
 
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
@@ -420,6 +451,9 @@ def main():
         result["compress"] = r["compress"]
     if args.path == "fused":
         result["pool_on_commit"] = {"ms_per_commit": round(leg.commit_ms, 4), "frames_per_commit": w.chunk_frames}
+    if not args.headline_only:
+        # the other path on the same inputs, after the timed region
+        result["paths"] = path_comparison(leg, r, K, args.warmup)
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 2
         src_t = torch.ones(n, dtype=torch.bfloat16, device="cuda")
@@ -518,6 +552,7 @@ def main():
             lg = Leg(wl, n_sets, args.path)
             rr = lg.time(steps, 2)
             extra[wl.name] = config_summary(lg, rr, steps)
+            extra[wl.name]["paths"] = path_comparison(lg, rr, steps, 2)
             del lg
             torch.cuda.empty_cache()
         result["configs"] = extra

@@ -151,6 +151,24 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
   const int64_t item = blockIdx.x;  // (b*H + h)*nqb + qb
   const int64_t bh = item / g.nqb;
   const int nb = g.nb, ns = g.ns;
+  constexpr int KV = QSlice<D>::SPAN / 4;
+
+  // Stage 1 key slices, kRoundsInFlight rounds of kPerRound frame candidates
+  // from candidate r0 on (lanes past the last candidate load the last one
+  // and drop it). The first batch is loaded before the query is read or
+  // pooled: it does not depend on it, so the two memory round trips overlap.
+  const int ncand = g.Fh - ns;
+  float4 kv1[kRoundsInFlight][KV];
+  const auto load_frames = [&](int r0) {
+#pragma unroll
+    for (int u = 0; u < kRoundsInFlight; ++u) {
+      if (r0 + u * kPerRound >= ncand) break;  // uniform: the whole wavefront skips
+      const int c = min(r0 + u * kPerRound + sub, ncand - 1);
+      QSlice<D>::load_key(k_frm + key_row(FUSED, g, bh, ns + c) * D, part, kv1[u]);
+    }
+  };
+  load_frames(0);
+
   if constexpr (FUSED) {
     using P = BlockPool<T, D>;
     const int qb = (int)(item - bh * g.nqb);
@@ -174,25 +192,16 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
 
   QSlice<D> qs;
   qs.load(qv, part);
-  constexpr int KV = QSlice<D>::SPAN / 4;
 
-  // Stage 1: frame scores (kPerRound candidates per round, kRoundsInFlight
-  // rounds loaded at once; lanes past the last candidate recompute the last
-  // one and drop it).
-  const int ncand = g.Fh - ns;
+  // Stage 1: frame scores, one batch of rounds at a time (the first batch
+  // is already in flight).
   for (int r0 = 0; r0 < ncand; r0 += kPerRound * kRoundsInFlight) {
-    float4 kv[kRoundsInFlight][KV];
-#pragma unroll
-    for (int u = 0; u < kRoundsInFlight; ++u) {
-      if (r0 + u * kPerRound >= ncand) break;  // uniform: the whole wavefront skips
-      const int c = min(r0 + u * kPerRound + sub, ncand - 1);
-      QSlice<D>::load_key(k_frm + key_row(FUSED, g, bh, ns + c) * D, part, kv[u]);
-    }
+    if (r0 > 0) load_frames(r0);
 #pragma unroll
     for (int u = 0; u < kRoundsInFlight; ++u) {
       if (r0 + u * kPerRound >= ncand) break;
       const int c = r0 + u * kPerRound + sub;
-      const double sc = qs.dot(kv[u]);
+      const double sc = qs.dot(kv1[u]);
       if (c < ncand && part == 0) fscore[c] = sc;
     }
   }
