@@ -216,6 +216,18 @@ lf_status lf_select(const lf_geom* g, const float* q_blk, const float* k_blk, co
                     "lf_select launch");
 }
 
+lf_status lf_check_selection(const lf_geom* g, const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel,
+                             int32_t* result, lf_stream stream) {
+  lf::KGeom kg;
+  lf_status st = make_geom(g, nullptr, &kg);
+  if (st != LF_OK) return st;
+  if (max_sel < 0 || max_sel > LF_MAX_SEL) return fail(LF_ERR_K, "max_sel must be in [0, LF_MAX_SEL]");
+  if (n_sel == nullptr || result == nullptr || (max_sel > 0 && sel_blocks == nullptr))
+    return fail(LF_ERR_NULL, "sel_blocks / n_sel / result is NULL");
+  return hip_status(lf::launch_check_selection(kg, sel_blocks, n_sel, max_sel, result, static_cast<hipStream_t>(stream)),
+                    "lf_check_selection launch");
+}
+
 lf_status lf_block_sparse_attn(const lf_geom* g, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* frame_slot, const int32_t* sel_blocks, const int32_t* n_sel,
                                int32_t max_sel, float softmax_scale, void* out, float* lse, lf_stream stream) {

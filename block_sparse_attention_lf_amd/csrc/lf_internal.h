@@ -35,6 +35,10 @@ hipError_t launch_select_fused(const KGeom& g, int32_t dtype, const void* q, con
                                hipStream_t stream);
 hipError_t launch_select_blocks(const KGeom& g, const float* q_blk, const float* k_blk, int32_t k,
                                 int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, hipStream_t stream);
+// Counts the selection rows that break the lists' invariants (result[0]) and
+// gives the first such row (result[1], -1 if none); one workgroup.
+hipError_t launch_check_selection(const KGeom& g, const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel,
+                                  int32_t* result, hipStream_t stream);
 hipError_t launch_attention(const KGeom& g, int32_t dtype, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel, float scale,
                             void* out, float* lse, hipStream_t stream);

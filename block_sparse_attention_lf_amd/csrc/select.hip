@@ -397,6 +397,73 @@ hipError_t launch_select_fused(const KGeom& g, int32_t dtype, const void* q, con
                                        max_sel, q_blk, stream);
 }
 
+namespace {
+
+// Selection-list check, one workgroup: wavefront w takes rows w, w + 16, ...
+// A row (b*H + h)*nqb + qb is bad when n_sel is outside [0, max_sel], or one
+// of its first n_sel ids is outside [0, Fh*nb), or an id is not greater than
+// the one before it. The count of bad rows and the smallest bad row (or -1)
+// are summed / taken in LDS and written by thread 0.
+constexpr int kCheckWaves = 16;
+__global__ __launch_bounds__(64 * kCheckWaves) void check_selection_kernel(const int32_t* __restrict__ sel,
+                                                                            const int32_t* __restrict__ n_sel,
+                                                                            int64_t rows, int max_sel, int n_ids,
+                                                                            int32_t* __restrict__ result) {
+  __shared__ int bad_count[kCheckWaves];
+  __shared__ int64_t first_bad[kCheckWaves];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int count = 0;
+  int64_t first = -1;
+  for (int64_t r = wv; r < rows; r += kCheckWaves) {
+    const int n = n_sel[r];
+    bool bad = n < 0 || n > max_sel;
+    if (!bad) {
+      const int32_t* ids = sel + r * max_sel;
+      for (int j0 = 0; j0 < n; j0 += 64) {
+        const int j = j0 + lane;
+        bool lane_bad = false;
+        if (j < n) {
+          const int x = ids[j];
+          lane_bad = x < 0 || x >= n_ids || (j > 0 && ids[j - 1] >= x);
+        }
+        if (__builtin_amdgcn_ballot_w64(lane_bad) != 0) {
+          bad = true;
+          break;
+        }
+      }
+    }
+    if (bad) {
+      ++count;
+      if (first < 0) first = r;
+    }
+  }
+  if (lane == 0) {
+    bad_count[wv] = count;
+    first_bad[wv] = first;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int total = 0;
+    int64_t lowest = -1;
+    for (int w = 0; w < kCheckWaves; ++w) {
+      total += bad_count[w];
+      if (first_bad[w] >= 0 && (lowest < 0 || first_bad[w] < lowest)) lowest = first_bad[w];
+    }
+    result[0] = total;
+    result[1] = (int32_t)lowest;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_check_selection(const KGeom& g, const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel,
+                                  int32_t* result, hipStream_t stream) {
+  const int64_t rows = (int64_t)g.B * g.H * g.nqb;
+  hipLaunchKernelGGL(check_selection_kernel, dim3(1), dim3(64 * kCheckWaves), 0, stream, sel_blocks, n_sel, rows,
+                     max_sel, g.Fh * g.nb, result);
+  return hipGetLastError();
+}
+
 hipError_t launch_select_blocks(const KGeom& g, const float* q_blk, const float* k_blk, int32_t k,
                                 int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)g.B * g.H * g.nqb);

@@ -30,7 +30,8 @@ STATUS = {0: "LF_OK", -1: "LF_ERR_NULL", -2: "LF_ERR_GEOM", -3: "LF_ERR_DTYPE", 
           -5: "LF_ERR_ALIGN", -6: "LF_ERR_HIP", -7: "LF_ERR_SLOT", -8: "LF_ERR_ARG"}
 
 # Every symbol include/lf.h declares.
-EXPORTS = ("lf_compress", "lf_max_sel", "lf_select", "lf_max_sel_1d", "lf_select_blocks", "lf_pool_keys", "lf_select_fused", "lf_block_sparse_attn",
+EXPORTS = ("lf_compress", "lf_max_sel", "lf_select", "lf_max_sel_1d", "lf_select_blocks", "lf_pool_keys",
+           "lf_select_fused", "lf_check_selection", "lf_block_sparse_attn",
            "lf_block_sparse_attn_fp8", "lf_block_sparse_attn_bwd", "lf_block_sparse_attn_bwd_noalloc",
            "lf_chunk_budget", "lf_cache_frame_slots", "lf_status_str", "lf_last_error", "lf_build_id")
 
@@ -95,6 +96,7 @@ def lib() -> ctypes.CDLL:
         "lf_select_fused": (ctypes.c_int, [G, _P, _P, _P, _I32P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                            ctypes.c_int32, _P, _P]),
         "lf_select_blocks": (ctypes.c_int, [G, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P]),
+        "lf_check_selection": (ctypes.c_int, [G, _P, _P, ctypes.c_int32, _P, _P]),
         "lf_block_sparse_attn": (ctypes.c_int, [G, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32, ctypes.c_float,
                                                 _P, _P, _P]),
         "lf_block_sparse_attn_fp8": (ctypes.c_int, [G, _P, _P, _P, _P, _P, _I32P, _P, _P, ctypes.c_int32,
@@ -247,6 +249,17 @@ def lf_select_blocks(g: lf_geom, q_blk, k_blk, k_total: int, sel_blocks, n_sel, 
     _need(n_sel, (g.batch, g.heads, g.n_qblocks), torch.int32, "n_sel")
     _check(lib().lf_select_blocks(ctypes.byref(g), _ptr(q_blk), _ptr(k_blk), k_total, _ptr(sel_blocks), _ptr(n_sel),
                                   max_sel, _stream(stream)), "lf_select_blocks")
+
+
+def lf_check_selection(g: lf_geom, sel_blocks, n_sel, result, stream=None) -> None:
+    """Debug check of selection lists (see include/lf.h): result (2 int32, device) gets the number of rows that
+    break the invariants and the first such row (-1 if none), on the stream."""
+    max_sel = sel_blocks.shape[-1]
+    _need(sel_blocks, (g.batch, g.heads, g.n_qblocks, max_sel), torch.int32, "sel_blocks")
+    _need(n_sel, (g.batch, g.heads, g.n_qblocks), torch.int32, "n_sel")
+    _need(result, (2,), torch.int32, "result")
+    _check(lib().lf_check_selection(ctypes.byref(g), _ptr(sel_blocks), _ptr(n_sel), max_sel, _ptr(result),
+                                    _stream(stream)), "lf_check_selection")
 
 
 def lf_block_sparse_attn(g: lf_geom, q, k_cache, v_cache, frame_slot, sel_blocks, n_sel, softmax_scale: float, out,

@@ -195,6 +195,23 @@ lf_status lf_select_blocks(const lf_geom* g, const float* q_blk, const float* k_
                            int32_t* sel_blocks, int32_t* n_sel, int32_t max_sel, lf_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * Debug check of selection lists against the invariants lf_select's output
+ * has ([LF-tech] 2.2, two-stage selection: a top-k of distinct blocks) and
+ * that lf_block_sparse_attn and lf_block_sparse_attn_bwd rely on (a block
+ * named twice in one list would be attended twice). For every (batch, head,
+ * query block) row r = (b*H + h)*nqb + qb: 0 <= n_sel[r] <= max_sel, and the
+ * first n_sel[r] ids of sel_blocks row r (row stride max_sel) are in
+ * [0, Fh*nb) and strictly ascending, hence distinct. Writes, on the stream,
+ * result[0] = the number of rows that break this and result[1] = the
+ * smallest such row, or -1 (result: 2 int32, device memory, caller-owned).
+ * One workgroup; the host is not synchronised (read result after the
+ * stream). max_sel must be in [0, LF_MAX_SEL]; NULL pointers give
+ * LF_ERR_NULL (sel_blocks may be NULL when max_sel is 0).
+ * ------------------------------------------------------------------------- */
+lf_status lf_check_selection(const lf_geom* g, const int32_t* sel_blocks, const int32_t* n_sel, int32_t max_sel,
+                             int32_t* result, lf_stream stream);
+
+/* ---------------------------------------------------------------------------
  * Block-sparse attention ([LF-tech] 2.2 "execution"; [LF-press] 3).
  * Each query row of query block qb attends, with softmax(scale * q k^T) v, to
  * the tokens of the history blocks sel_blocks[qb][0 .. n_sel[qb]-1] and to

@@ -164,6 +164,20 @@ def test_select_blocks_validation():
     assert L.lf_select_blocks(ctypes.byref(big), p, p, 30, p, p, 10 ** 6, None) == -2
 
 
+def test_check_selection_validation():
+    g = lf.geom_of(I.WAN480P_CHUNK)
+    L = lf.lib()
+    p = ctypes.c_void_p(4096)
+    assert L.lf_check_selection(ctypes.byref(g), p, p, -1, p, None) == -4
+    assert L.lf_check_selection(ctypes.byref(g), p, p, 100000, p, None) == -4
+    assert L.lf_check_selection(ctypes.byref(g), p, None, 30, p, None) == -1
+    assert L.lf_check_selection(ctypes.byref(g), p, p, 30, None, None) == -1
+    assert L.lf_check_selection(ctypes.byref(g), None, p, 30, p, None) == -1
+    bad = lf.geom_of(I.WAN480P_CHUNK)
+    bad.block = 0
+    assert L.lf_check_selection(ctypes.byref(bad), p, p, 30, p, None) == -2
+
+
 def test_pool_keys_validation():
     w = I.WAN480P_CHUNK
     g = lf.geom_of(w)
