@@ -25,8 +25,10 @@
 //     write LDS directly (16 bytes per lane, no registers). Each tile's
 //     buffer resource covers only its valid rows, so rows past the end of a
 //     ragged block read as zeros (then masked) and no load leaves the tile.
-//     LDS rows are padded so the fragment reads spread over the banks and
-//     every fragment address is one per-lane base plus a constant.
+//     LDS rows of bf16 keys and values at d = 128 are 256 bytes with their
+//     16-byte chunks XOR-swizzled per row (lds_swizzle), other rows are
+//     padded; either way the fragment reads spread over the banks and every
+//     fragment address is one per-lane base XOR (or plus) a constant.
 //   * MFMA 32x32x16 bf16 (32x32x2 f32 for fp32 inputs). Scores are formed
 //     transposed, S^T = K Q^T (A = K from LDS, B = this wavefront's 32
 //     queries, kept in registers for the whole walk), so each lane holds one
@@ -104,7 +106,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // Q8 (bf16 walks only): queries and keys arrive as E4M3 codes with one E8M0
 // scale per 32 channels of a token; the scores are formed with the scaled
 // FP8 MFMA (32x32x64), everything after them as in the bf16 walk.
-template <typename T, int D, int WPQ, int QPWT = 4 / WPQ, bool SPLIT_PITCH = false, bool Q8 = false>
+template <typename T, int D, int WPQ, int QPWT = 4 / WPQ, bool Q8 = false>
 struct Walk {
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -113,18 +115,11 @@ struct Walk {
   static constexpr int NT = 64 * NW;
   static constexpr int ES = (int)sizeof(T);
   static constexpr int CPR = D * ES / 16;          // 16-byte chunks per key row
-  // LDS rows are padded so that the fragment reads of a wavefront spread
-  // over the banks, and every fragment address is one per-lane base plus a
-  // compile-time offset. K and V tiles are read differently (16-byte reads
-  // of 32 rows for K; transposing 8-byte reads that gather 4 row pieces of
-  // 32 bytes per 16 lanes for V), and no single pitch suits both: for
-  // 256-byte rows (bf16, D = 128) a 16-byte pad makes the K reads and a
-  // 64-byte pad the V reads conflict-free (measured on gfx950; the shared
-  // 32-byte pad costs both about a third of their LDS throughput). The
-  // double-buffered walk takes the split pitches; the single-stage walk
-  // keeps 32 bytes for both, since there the wider V rows' extra load
-  // instruction and pad traffic cost more than the conflicts (measured).
-  static constexpr bool kSplitPitch = SPLIT_PITCH && ES == 2 && D == 128;
+  // LDS row layout. K and V tiles are read differently (16-byte reads of 32
+  // rows for K; transposing 8-byte reads that gather 4 row pieces of 32
+  // bytes per 16 lanes for V). Rows other than those below are padded by 32
+  // bytes, which spreads both reads over the banks well enough at those
+  // sizes, and every fragment address is one per-lane base plus a constant.
   static constexpr int KES = Q8 ? 1 : ES;                       // bytes per key element
   static constexpr int CPRK = D * KES / 16;                     // 16-byte chunks per key row
   // bf16 rows of 256 bytes (D = 128) are stored unpadded with the 16-byte
@@ -140,8 +135,8 @@ struct Walk {
   static constexpr bool kSwzV = ES == 2 && D == 128;
   // (FP8 key rows: 16-byte pad, the two 16-byte reads per lane of a row
   // then fall in distinct bank groups)
-  static constexpr int RSK = kSwzK ? 256 : D * KES + (Q8 ? 16 : (kSplitPitch ? 16 : 32));  // K row pitch in bytes
-  static constexpr int RSV = kSwzV ? 256 : D * ES + (kSplitPitch ? 64 : 32);  // V row pitch in bytes
+  static constexpr int RSK = kSwzK ? 256 : D * KES + (Q8 ? 16 : 32);  // K row pitch in bytes
+  static constexpr int RSV = kSwzV ? 256 : D * ES + 32;                // V row pitch in bytes
   static constexpr int SPRK = RSK / 16, SPRV = RSV / 16;       // 16-byte slots per row (CPR data + pad)
   static constexpr int SLOTS_K = BN * SPRK, SLOTS_V = BN * SPRV;
   static constexpr int LIK = (SLOTS_K + NT - 1) / NT;          // load instructions per wavefront per K tile
@@ -874,7 +869,7 @@ __global__ __launch_bounds__((64 * WPQ * (SS ? 1 : 4 / WPQ)), (WAVES_PER_SIMD<T,
     const int32_t* __restrict__ nsel, int max_sel, float scale, const KGeom g, T* __restrict__ out,
     float* __restrict__ lse, const Fp8Operands f8) {
   static_assert(!Q8 || (D == 128 && sizeof(T) == 2), "FP8 scores: bf16 values, D = 128");
-  using W = Walk<T, D, WPQ, SS ? 1 : 4 / WPQ, !SS, Q8>;
+  using W = Walk<T, D, WPQ, SS ? 1 : 4 / WPQ, Q8>;
   constexpr int QPW = W::QPW, ES = W::ES, QSTEPS = W::QSTEPS, DB = W::DB;
 
   // Two named stage buffers (not one indexed array): the loop below is
