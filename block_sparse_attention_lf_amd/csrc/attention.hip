@@ -232,8 +232,6 @@ struct Walk {
     char* kd;
     char* vd;
   };
-  // Buffer resource word 3 for raw (untyped) dword access on this GPU family.
-  static constexpr int kRawBufferFlags = 0x00020000;
   // When the walk has no next tile the caller passes the last one again: it
   // is re-read into the idle buffer, which nothing reads any more (cheaper
   // than a branch around every load).
