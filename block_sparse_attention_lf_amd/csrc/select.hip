@@ -14,12 +14,12 @@
 // larger, or equal with a lower index. That is exactly "stable sort
 // descending, take the first k" without sorting.
 //
-// Design: one wavefront per (batch, head, query block). Each dot product is
-// shared by 8 lanes (each holds its D/8 channels of the pooled query in
-// registers; the partial sums meet through DPP lane moves), so a wavefront
-// scores 8 candidates per round with dependent chains of D/8 fused
-// multiply-adds, and the key slices of four rounds are loaded before any is
-// summed. The frame candidates are scored, ranked against the scores
+// Design: one workgroup of two wavefronts per (batch, head, query block).
+// Each dot product is shared by 8 lanes (each holds its D/8 channels of the
+// pooled query in registers; the partial sums meet through DPP lane moves),
+// so a workgroup scores 16 candidates per round with dependent chains of D/8
+// fused multiply-adds, and the key slices of four rounds are loaded before
+// any is summed. The frame candidates are scored, ranked against the scores
 // kept in LDS, and then the blocks of all kept frames are scored as one batch
 // (up to 1024 at a time) and ranked inside their frame; kept ids are
 // compacted in ascending order with a ballot and a prefix popcount. The whole
@@ -49,6 +49,9 @@ __device__ inline double dot_f64(const float* __restrict__ qv_lds, const float* 
 constexpr int kDotLanes = 8;
 constexpr int kPerRound = 64 / kDotLanes;
 constexpr int kBlockBatch = 1024;
+// Wavefronts per query block in the two-stage selection (two measured
+// 4-11% faster than one; four leave too few workgroups resident per CU).
+constexpr int kSelectWaves = 2;
 static_assert(LF_MAX_BLOCKS_PER_FRAME <= kBlockBatch, "one frame's blocks must fit a batch");
 
 // v of another lane of the same row of 16 lanes, moved by the DPP control
@@ -107,15 +110,16 @@ struct QSlice {
 // Rounds of kPerRound candidates whose key slices are in flight together.
 constexpr int kRoundsInFlight = 4;
 
-// keep[c] = 1 iff fewer than k candidates rank above c.
-__device__ inline void rank_keep(const double* score, int n, int k, unsigned char* keep, int lane) {
-  for (int c = lane; c < n; c += 64) {
+// keep[c] = 1 iff fewer than k candidates rank above c (thread t of nt
+// takes c = t, t + nt, ...).
+__device__ inline void rank_keep(const double* score, int n, int k, unsigned char* keep, int t, int nt) {
+  for (int c = t; c < n; c += nt) {
     const double s = score[c];
     int above = 0;
 #pragma unroll 8
     for (int i = 0; i < n; ++i) {
-      const double t = score[i];
-      above += (t > s) || (t == s && i < c);
+      const double v = score[i];
+      above += (v > s) || (v == s && i < c);
     }
     keep[c] = above < k;
   }
@@ -131,39 +135,48 @@ __device__ inline int64_t key_row(bool by_slot, const KGeom& g, int64_t bh, int 
 // FUSED = false: pooled queries q_blk and pooled keys per logical history
 // frame, as lf_compress writes them. FUSED = true: the query block is pooled
 // here from q (and optionally written to q_blk_out), and the pooled keys come
-// from the slot-indexed cache filled on commit.
-template <int D, bool FUSED, typename T>
-__global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_blk, const T* __restrict__ q,
-                                                    const float* __restrict__ k_blk, const float* __restrict__ k_frm,
-                                                    const KGeom g, int kf, int kb, int kf_stride,
-                                                    int32_t* __restrict__ sel_frames,
-                                                    int32_t* __restrict__ sel_blocks, int32_t* __restrict__ n_sel,
-                                                    int max_sel, float* __restrict__ q_blk_out) {
+// from the slot-indexed cache filled on commit. NWS wavefronts per query
+// block: a round scores kPerRound candidates per wavefront, and the bf16
+// query block's rows are split between the wavefronts (float64 partial sums
+// of bf16 values are exact, so the split does not change the mean; float32
+// queries are pooled by one wavefront, in lf_compress's order).
+template <int D, bool FUSED, typename T, int NWS>
+__global__ __launch_bounds__(64 * NWS) void select_kernel(const float* __restrict__ q_blk, const T* __restrict__ q,
+                                                          const float* __restrict__ k_blk,
+                                                          const float* __restrict__ k_frm, const KGeom g, int kf,
+                                                          int kb, int kf_stride, int32_t* __restrict__ sel_frames,
+                                                          int32_t* __restrict__ sel_blocks,
+                                                          int32_t* __restrict__ n_sel, int max_sel,
+                                                          float* __restrict__ q_blk_out) {
+  constexpr int NT = 64 * NWS;
+  constexpr int PR = kPerRound * NWS;  // candidates per round
   __shared__ __attribute__((aligned(16))) float qv[D];
   __shared__ double fscore[LF_MAX_FRAMES];
   __shared__ unsigned char fkeep[LF_MAX_FRAMES];
   __shared__ double bscore[kBlockBatch];
   __shared__ unsigned char bkeep[kBlockBatch];
   __shared__ int bframe[LF_MAX_FRAMES];
+  __shared__ double qpart[FUSED && NWS > 1 ? NWS : 1][FUSED && NWS > 1 ? D : 1];
 
-  const int lane = threadIdx.x;
-  const int part = lane % kDotLanes, sub = lane / kDotLanes;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int part = lane % kDotLanes, sub = wv * kPerRound + lane / kDotLanes;  // candidate slot in a round
   const int64_t item = blockIdx.x;  // (b*H + h)*nqb + qb
   const int64_t bh = item / g.nqb;
   const int nb = g.nb, ns = g.ns;
   constexpr int KV = QSlice<D>::SPAN / 4;
 
-  // Stage 1 key slices, kRoundsInFlight rounds of kPerRound frame candidates
-  // from candidate r0 on (lanes past the last candidate load the last one
-  // and drop it). The first batch is loaded before the query is read or
-  // pooled: it does not depend on it, so the two memory round trips overlap.
+  // Stage 1 key slices, kRoundsInFlight rounds of PR frame candidates from
+  // candidate r0 on (lanes past the last candidate load the last one and
+  // drop it). The first batch is loaded before the query is read or pooled:
+  // it does not depend on it, so the two memory round trips overlap.
   const int ncand = g.Fh - ns;
   float4 kv1[kRoundsInFlight][KV];
   const auto load_frames = [&](int r0) {
 #pragma unroll
     for (int u = 0; u < kRoundsInFlight; ++u) {
-      if (r0 + u * kPerRound >= ncand) break;  // uniform: the whole wavefront skips
-      const int c = min(r0 + u * kPerRound + sub, ncand - 1);
+      if (r0 + u * PR + wv * kPerRound >= ncand) break;  // uniform over the wavefront
+      const int c = min(r0 + u * PR + sub, ncand - 1);
       QSlice<D>::load_key(k_frm + key_row(FUSED, g, bh, ns + c) * D, part, kv1[u]);
     }
   };
@@ -174,50 +187,75 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
     const int qb = (int)(item - bh * g.nqb);
     const int fc = qb / nb, jq = qb - fc * nb;
     const int rows = min(g.b, g.T - jq * g.b);
-    double acc[P::EPL];
-    P::sums(q + (bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b) * D, rows, lane, acc);
-    if (lane < P::LPR) {
+    const T* src = q + (bh * g.Lq + (int64_t)fc * g.T + (int64_t)jq * g.b) * D;
+    if constexpr (NWS > 1 && sizeof(T) == 2) {
+      // wavefront w sums rows [w*RW, w*RW + RW) (RW a multiple of a load's rows)
+      const int per = (rows + NWS - 1) / NWS;
+      const int RW = (per + P::RPL - 1) / P::RPL * P::RPL;
+      const int r0 = wv * RW, nr = max(0, min(RW, rows - r0));
+      double acc[P::EPL];
+      P::sums(src + (int64_t)r0 * D, nr, lane, acc);
+      if (lane < P::LPR) {
 #pragma unroll
-      for (int e = 0; e < P::EPL; ++e) qv[lane * P::EPL + e] = (float)(acc[e] / (double)rows);
+        for (int e = 0; e < P::EPL; ++e) qpart[wv][lane * P::EPL + e] = acc[e];
+      }
+      __syncthreads();
+      for (int d = tid; d < D; d += NT) {
+        double t = 0.0;
+#pragma unroll
+        for (int w = 0; w < NWS; ++w) t += qpart[w][d];
+        const float m = (float)(t / (double)rows);
+        qv[d] = m;
+        if (q_blk_out != nullptr) q_blk_out[item * D + d] = m;
+      }
+    } else {
+      if (wv == 0) {
+        double acc[P::EPL];
+        P::sums(src, rows, lane, acc);
+        if (lane < P::LPR) {
+#pragma unroll
+          for (int e = 0; e < P::EPL; ++e) qv[lane * P::EPL + e] = (float)(acc[e] / (double)rows);
+        }
+        if (q_blk_out != nullptr) P::store_mean(q_blk_out + item * D, acc, rows, lane);
+      }
     }
-    if (q_blk_out != nullptr) P::store_mean(q_blk_out + item * D, acc, rows, lane);
   } else {
-    for (int d = lane; d < D; d += 64) qv[d] = q_blk[item * D + d];
+    for (int d = tid; d < D; d += NT) qv[d] = q_blk[item * D + d];
   }
   __syncthreads();
 
   int32_t* out = sel_blocks + item * max_sel;
-  for (int i = lane; i < ns * nb; i += 64) out[i] = i;  // sink frames in full
-  int pos = ns * nb;
+  for (int i = tid; i < ns * nb; i += NT) out[i] = i;  // sink frames in full
+  int pos = ns * nb;  // (kept by wavefront 0, which writes the kept ids)
 
   QSlice<D> qs;
   qs.load(qv, part);
 
   // Stage 1: frame scores, one batch of rounds at a time (the first batch
   // is already in flight).
-  for (int r0 = 0; r0 < ncand; r0 += kPerRound * kRoundsInFlight) {
+  for (int r0 = 0; r0 < ncand; r0 += PR * kRoundsInFlight) {
     if (r0 > 0) load_frames(r0);
 #pragma unroll
     for (int u = 0; u < kRoundsInFlight; ++u) {
-      if (r0 + u * kPerRound >= ncand) break;
-      const int c = r0 + u * kPerRound + sub;
+      if (r0 + u * PR + wv * kPerRound >= ncand) break;
+      const int c = r0 + u * PR + sub;
       const double sc = qs.dot(kv1[u]);
       if (c < ncand && part == 0) fscore[c] = sc;
     }
   }
   __syncthreads();
-  rank_keep(fscore, ncand, kf, fkeep, lane);
+  rank_keep(fscore, ncand, kf, fkeep, tid, NT);
   __syncthreads();
 
   // Stage 2: the blocks of the kept frames, in batches of whole frames.
   int c = 0, nf = 0;
   for (;;) {
-    int nbf = 0;  // kept frames in this batch (uniform across lanes)
+    int nbf = 0;  // kept frames in this batch (uniform across the workgroup)
     while (c < ncand && (nbf + 1) * nb <= kBlockBatch) {
       if (fkeep[c]) {
         const int f = ns + c;
-        if (lane == 0) bframe[nbf] = f;
-        if (sel_frames != nullptr && lane == 0 && nf < kf_stride) sel_frames[item * kf_stride + nf] = f;
+        if (tid == 0) bframe[nbf] = f;
+        if (sel_frames != nullptr && tid == 0 && nf < kf_stride) sel_frames[item * kf_stride + nf] = f;
         ++nbf;
         ++nf;
       }
@@ -226,25 +264,25 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
     if (nbf == 0) break;
     __syncthreads();  // bframe is visible
     const int nc = nbf * nb;
-    for (int r0 = 0; r0 < nc; r0 += kPerRound * kRoundsInFlight) {
+    for (int r0 = 0; r0 < nc; r0 += PR * kRoundsInFlight) {
       float4 kv[kRoundsInFlight][KV];
 #pragma unroll
       for (int u = 0; u < kRoundsInFlight; ++u) {
-        if (r0 + u * kPerRound >= nc) break;  // uniform: the whole wavefront skips
-        const int xc = min(r0 + u * kPerRound + sub, nc - 1);
+        if (r0 + u * PR + wv * kPerRound >= nc) break;  // uniform over the wavefront
+        const int xc = min(r0 + u * PR + sub, nc - 1);
         const int fi = xc / nb, j = xc - fi * nb;
         QSlice<D>::load_key(k_blk + (key_row(FUSED, g, bh, bframe[fi]) * nb + j) * (int64_t)D, part, kv[u]);
       }
 #pragma unroll
       for (int u = 0; u < kRoundsInFlight; ++u) {
-        if (r0 + u * kPerRound >= nc) break;
-        const int x = r0 + u * kPerRound + sub;
+        if (r0 + u * PR + wv * kPerRound >= nc) break;
+        const int x = r0 + u * PR + sub;
         const double sc = qs.dot(kv[u]);
         if (x < nc && part == 0) bscore[x] = sc;
       }
     }
     __syncthreads();
-    for (int x = lane; x < nc; x += 64) {  // rank inside the candidate's frame
+    for (int x = tid; x < nc; x += NT) {  // rank inside the candidate's frame
       const int fi = x / nb, j = x - fi * nb;
       const double* seg = bscore + fi * nb;
       const double sc = seg[j];
@@ -257,23 +295,27 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ q_
       bkeep[x] = above < kb;
     }
     __syncthreads();
-    for (int x0 = 0; x0 < nc; x0 += 64) {
-      const int x = x0 + lane;
-      const bool take = x < nc && bkeep[x];
-      const unsigned long long m = __ballot(take);
-      const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
-      if (take && at < max_sel) {  // bound holds unless scores are NaN
-        const int fi = x / nb;
-        out[at] = bframe[fi] * nb + (x - fi * nb);
+    if (wv == 0) {
+      for (int x0 = 0; x0 < nc; x0 += 64) {
+        const int x = x0 + lane;
+        const bool take = x < nc && bkeep[x];
+        const unsigned long long m = __ballot(take);
+        const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
+        if (take && at < max_sel) {  // bound holds unless scores are NaN
+          const int fi = x / nb;
+          out[at] = bframe[fi] * nb + (x - fi * nb);
+        }
+        pos = min(pos + __popcll(m), max_sel);
       }
-      pos = min(pos + __popcll(m), max_sel);
     }
     __syncthreads();  // bframe/bscore/bkeep are rewritten by the next batch
   }
   if (sel_frames != nullptr)
-    for (int i = nf + lane; i < kf_stride; i += 64) sel_frames[item * kf_stride + i] = -1;
-  for (int i = pos + lane; i < max_sel; i += 64) out[i] = -1;
-  if (lane == 0) n_sel[item] = pos;
+    for (int i = nf + tid; i < kf_stride; i += NT) sel_frames[item * kf_stride + i] = -1;
+  if (wv == 0) {
+    for (int i = pos + lane; i < max_sel; i += 64) out[i] = -1;
+    if (lane == 0) n_sel[item] = pos;
+  }
 }
 
 // Order-preserving map of a float64 score to an unsigned key (larger score,
@@ -357,10 +399,10 @@ hipError_t launch_select(const KGeom& g, const float* q_blk, const float* k_blk,
   const unsigned grid = (unsigned)((int64_t)g.B * g.H * g.nqb);
   const float* no_q = nullptr;
   if (g.D == 128)
-    hipLaunchKernelGGL((select_kernel<128, false, float>), dim3(grid), dim3(64), 0, stream, q_blk, no_q, k_blk, k_frm,
+    hipLaunchKernelGGL((select_kernel<128, false, float, kSelectWaves>), dim3(grid), dim3(64 * kSelectWaves), 0, stream, q_blk, no_q, k_blk, k_frm,
                        g, kf, kb, k_frames_stride, sel_frames, sel_blocks, n_sel, max_sel, nullptr);
   else
-    hipLaunchKernelGGL((select_kernel<64, false, float>), dim3(grid), dim3(64), 0, stream, q_blk, no_q, k_blk, k_frm,
+    hipLaunchKernelGGL((select_kernel<64, false, float, kSelectWaves>), dim3(grid), dim3(64 * kSelectWaves), 0, stream, q_blk, no_q, k_blk, k_frm,
                        g, kf, kb, k_frames_stride, sel_frames, sel_blocks, n_sel, max_sel, nullptr);
   return hipGetLastError();
 }
@@ -372,7 +414,7 @@ hipError_t launch_fused_typed(const KGeom& g, const void* q, const float* kp_blk
                               int32_t* n_sel, int32_t max_sel, float* q_blk, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)g.B * g.H * g.nqb);
   const float* no_qblk = nullptr;
-  hipLaunchKernelGGL((select_kernel<D, true, T>), dim3(grid), dim3(64), 0, stream, no_qblk, static_cast<const T*>(q),
+  hipLaunchKernelGGL((select_kernel<D, true, T, kSelectWaves>), dim3(grid), dim3(64 * kSelectWaves), 0, stream, no_qblk, static_cast<const T*>(q),
                      kp_blk, kp_frm, g, kf, kb, k_frames_stride, sel_frames, sel_blocks, n_sel, max_sel, q_blk);
   return hipGetLastError();
 }
