@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--cpu-single-thread", action="store_true",
                     help="also time the oracle on one thread on the tiny fp32 case and the 480p chunk")
     ap.add_argument("--cpu-sample-qblocks", type=int, default=0, help="0: every query block (the whole call)")
+    ap.add_argument("--dense-vs-sdpa", action="store_true",
+                    help="also time dense attention (no history) against torch's scaled_dot_product_attention "
+                         "(flash and memory-efficient backends) at the chunk shapes; report under 'dense_vs_sdpa'")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one elementwise kernel that reads and writes this many MiB "
                          "(a known-size reference for hardware byte counters)")
@@ -171,6 +174,62 @@ def rollout(warmup: int):
             "total_effective_gflop": round(tot_flops / 1e9, 1),
             "tflops": round(tot_flops / (tot_ms * 1e-3) / 1e12, 1), "beta": round(float(bud["beta"]), 6),
             "chunks": chunks}
+
+
+def dense_vs_sdpa(warmup: int, steps: int):
+    """Dense attention of a chunk over itself (no history: every query block sees every key) through
+    lf_block_sparse_attn, beside torch's scaled_dot_product_attention on the same bf16 tensors with only its
+    flash and memory-efficient backends enabled. Shapes: the 480p chunk (12 heads, 3 frames of 1560 tokens),
+    twice as many frames, and the wide head's 40 heads. HIP events on the current stream, medians."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    from block_sparse_attention_lf_amd import lf
+
+    stream = torch.cuda.current_stream()
+
+    def med_ms(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    rows = []
+    for heads, frames, tpf, d in ((12, 3, 1560, 128), (12, 6, 1560, 128), (40, 3, 1560, 128)):
+        n = frames * tpf
+        flops = 4.0 * n * n * d * heads
+        gen = torch.Generator().manual_seed(1234 + heads + frames)
+        q, k, v = (torch.randn(1, heads, n, d, generator=gen).to(torch.bfloat16).cuda() for _ in range(3))
+        g = lf.make_geom(1, heads, d, tpf, 64, frames, 0, 0, frames, "bf16")
+        kc, vc = k.view(1, heads, frames, tpf, d), v.view(1, heads, frames, tpf, d)
+        out = torch.empty_like(q)
+        slots = np.arange(frames, dtype=np.int32)
+        t_lf = med_ms(lambda: lf.lf_block_sparse_attn(g, q, kc, vc, slots, None, None, 1.0 / math.sqrt(d), out,
+                                                      None, stream))
+        row = {"heads": heads, "tokens": n, "head_dim": d, "flops": flops, "lf_us": round(t_lf * 1e3, 1),
+               "lf_tflops": round(flops / (t_lf * 1e-3) / 1e12, 1)}
+        for name, be in (("flash", SDPBackend.FLASH_ATTENTION), ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+            try:
+                with sdpa_kernel([be]):
+                    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+                    t = med_ms(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v))
+                row[f"sdpa_{name}_us"] = round(t * 1e3, 1)
+                row[f"sdpa_{name}_tflops"] = round(flops / (t * 1e-3) / 1e12, 1)
+                row[f"max_abs_diff_vs_sdpa_{name}"] = float((out.float() - ref.float()).abs().max().item())
+            except RuntimeError as e:  # backend not built for this device
+                row[f"sdpa_{name}"] = f"unavailable: {str(e)[:120]}"
+        rows.append(row)
+        del q, k, v, kc, vc, out
+        torch.cuda.empty_cache()
+    return rows
 
 
 def cpu_baseline(w, x, k_frames, k_blocks, sample_qblocks: int):
@@ -539,6 +598,9 @@ def main():
                          "frac_of_bf16_peak": round(fach / PEAK_BF16_TFLOPS, 4),
                          "speedup_vs_bf16_attention": round(attn_ms / fms, 3),
                          "kernel": "attn_kernel Q8 (lf_block_sparse_attn_fp8)"}
+    if args.dense_vs_sdpa:
+        print("[bench] dense attention against torch SDPA", file=sys.stderr, flush=True)
+        result["dense_vs_sdpa"] = dense_vs_sdpa(max(args.warmup, 2), max(K, 5))
     if not args.headline_only:
         # The other workloads on the same clock: long history with a sink and the
         # wide-head case (one input set each beyond what the MALL holds), then
