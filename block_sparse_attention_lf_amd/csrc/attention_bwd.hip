@@ -471,8 +471,8 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
                                                       const float* __restrict__ lse, const float* __restrict__ delta,
                                                       const int32_t* __restrict__ sel,
                                                       const int32_t* __restrict__ nsel, int max_sel, float scale,
-                                                      const KGeom g, float* __restrict__ dv,
-                                                      float* __restrict__ dk) {
+                                                      const KGeom g, const int* __restrict__ order,
+                                                      float* __restrict__ dv, float* __restrict__ dk) {
   using S = BwdShape<D>;
   constexpr int NT = 64 * NW;
   constexpr int KEYS = 32 * NW;  // keys per workgroup
@@ -491,7 +491,8 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
   const int hpb = g.b > 64 ? 2 : 1;
   const int gpf = (g.T + KEYS - 1) / KEYS;  // key groups per current frame
   const int per_bh = CUR ? g.Fc * gpf : g.Fh * g.nb * hpb;
-  const int wgi = xcd_item(blockIdx.x, gridDim.x);
+  const int wgx = xcd_item(blockIdx.x, gridDim.x);
+  const int wgi = !CUR && order != nullptr ? order[wgx] : wgx;  // history: longest first (hist_order_kernel)
   const int64_t bh = wgi / per_bh;
   const int ti = (int)(wgi - bh * per_bh);
   int f, start, count, hist_id = -1;
@@ -655,6 +656,73 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 || MAXQ <= 32 ? 2 : 1)) void bwd_
   }
 }
 
+// Launch order of the history dK/dV pass, longest first. A history tile's
+// workgroup walks the query blocks whose selections name its block, so its
+// time grows with their number (1 to 28 at the 480p workload). Workgroups
+// are dealt round-robin to the 8 XCDs and each XCD works through one
+// contiguous range of items (xcd_item); this kernel permutes each range so
+// that its items come in descending order of that number, and the pass
+// takes item order[xcd_item(wg)]. The longest workgroups then start first
+// and the pass does not end on a few long ones started late (list
+// scheduling, longest first). It decides only when each workgroup runs,
+// not what any of them computes. One workgroup per range: count in LDS,
+// then a counting sort by count.
+constexpr int kOrderMaxItems = 12288;  // items per range (LDS); larger passes keep the plain order
+constexpr int kOrderBuckets = 1024;    // counts are clamped to kOrderBuckets - 1
+
+__global__ __launch_bounds__(1024) void hist_order_kernel(const int32_t* __restrict__ sel,
+                                                          const int32_t* __restrict__ nsel, int max_sel, const KGeom g,
+                                                          int nitems, int* __restrict__ order) {
+  __shared__ int cnt[kOrderMaxItems];
+  __shared__ int base[kOrderBuckets];
+  const int x = blockIdx.x, tid = threadIdx.x;
+  const int per = nitems >> 3, rem = nitems & 7;
+  const int lo = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  const int n = per + (x < rem ? 1 : 0);
+  if (n <= 0) return;
+  for (int i = tid; i < n; i += 1024) cnt[i] = 0;
+  for (int i = tid; i < kOrderBuckets; i += 1024) base[i] = 0;
+  __syncthreads();
+  const int hpb = g.b > 64 ? 2 : 1, nblk = g.Fh * g.nb, per_bh = nblk * hpb;
+  const int n_ent = g.nqb * max_sel;
+  for (int bh = lo / per_bh; bh <= (lo + n - 1) / per_bh; ++bh) {
+    const int32_t* rows = sel + (int64_t)bh * n_ent;
+    for (int e = tid; e < n_ent; e += 1024) {
+      const int qi = e / max_sel;
+      const int len = min(max(nsel[(int64_t)bh * g.nqb + qi], 0), max_sel);
+      const int id = rows[e];
+      if (e - qi * max_sel < len && id >= 0 && id < nblk)
+        for (int hf = 0; hf < hpb; ++hf) {
+          const int it = bh * per_bh + id * hpb + hf - lo;
+          if (it >= 0 && it < n) atomicAdd(&cnt[it], 1);
+        }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) atomicAdd(&base[min(cnt[i], kOrderBuckets - 1)], 1);
+  __syncthreads();
+  if (tid < 64) {
+    // bucket starts in descending count order: lane l takes the 16 buckets
+    // below kOrderBuckets - 16 l, then an exclusive scan over the lanes
+    const int top = kOrderBuckets - 16 * tid;
+    int sum = 0;
+    for (int c = top - 1; c >= top - 16; --c) sum += base[c];
+    int incl = sum;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (tid >= off) incl += t;
+    }
+    int run = incl - sum;
+    for (int c = top - 1; c >= top - 16; --c) {
+      const int t = base[c];
+      base[c] = run;
+      run += t;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) order[lo + atomicAdd(&base[min(cnt[i], kOrderBuckets - 1)], 1)] = lo + i;
+}
+
 // Key tile width of the dQ walk (32: two wavefronts per SIMD; 64: one, with
 // half the tiles).
 constexpr int kDqKeys = 32;
@@ -695,13 +763,23 @@ hipError_t launch_bwd_d(const KGeom& g, const void* q, const void* k, const void
   // The eight-wavefront current workgroups fill a CU on their own and
   // stage up to 64 query rows per step (78 KB of LDS); the two-wavefront
   // history workgroups stage 32 rows per step (40 KB), so four share a CU.
+  // The history pass runs first, in the order hist_order_kernel writes into
+  // the dk rows of the first chunk frame of (batch 0, head 0): T * D floats
+  // that the current-chunk pass overwrites with their gradients afterwards,
+  // so the call needs no scratch for it.
   const unsigned ncur = (unsigned)((int64_t)g.B * g.H * g.Fc * ((g.T + 255) / 256));
   const unsigned nhist = (unsigned)((int64_t)g.B * g.H * g.Fh * g.nb * (g.b > 64 ? 2 : 1));
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, 64, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta, sel,
-                     nsel, max_sel, scale, g, dv, dk);
-  if (nhist > 0)
+  if (nhist > 0) {
+    int* order = nullptr;
+    if (max_sel > 0 && (nhist + 7) / 8 <= (unsigned)kOrderMaxItems && (int64_t)nhist <= (int64_t)g.T * D) {
+      order = reinterpret_cast<int*>(dk + (int64_t)g.slot[g.Fh] * g.T * D);
+      hipLaunchKernelGGL(hist_order_kernel, dim3(8), dim3(1024), 0, stream, sel, nsel, max_sel, g, (int)nhist, order);
+    }
     hipLaunchKernelGGL((bwd_dkv_kernel<D, 32, 2, false>), dim3(nhist), dim3(128), 0, stream, Q, K, V, G, lse, delta,
-                       sel, nsel, max_sel, scale, g, dv, dk);
+                       sel, nsel, max_sel, scale, g, order, dv, dk);
+  }
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, 64, 8, true>), dim3(ncur), dim3(512), 0, stream, Q, K, V, G, lse, delta, sel,
+                     nsel, max_sel, scale, g, nullptr, dv, dk);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ def _check(name, got, want):
     assert rel <= REL_L2 and mx <= MAX_REL, (name, rel, mx)
 
 
-def _run(w, heads_checked=None, seed=17):
+def _run(w, heads_checked=None, seed=17, sel_fn=None):
     _say(f"[bwd] {w.name} B={w.batch} H={w.heads} d={w.head_dim} T={w.tokens_per_frame} b={w.block} "
          f"Fc={w.chunk_frames} Fh={w.hist_frames}")
     x = I.make_inputs(w)
@@ -50,6 +50,8 @@ def _run(w, heads_checked=None, seed=17):
     dev = P.device_inputs(w, x)
     q, kc, vc = dev
     _, s = P.oracle_compress_select(w, x, w.k_frames, w.k_blocks)
+    if sel_fn is not None:
+        s = sel_fn(w, s)
     sb = torch.from_numpy(np.ascontiguousarray(s["sel_blocks"], np.int32)).cuda()
     ns = torch.from_numpy(np.ascontiguousarray(s["n_sel"], np.int32)).cuda()
     scale = 1.0 / math.sqrt(w.head_dim)
@@ -100,6 +102,33 @@ def test_backward_empty_history():
 def test_backward_wan480p_shape_two_heads():
     """The 480p chunk's shapes (T=1560, b=64, Fc=3, Fh=6, 80%) on unit-normal inputs; heads 0-1 checked."""
     _run(I.WAN480P_CHUNK.replace(dist="normal", seed=11), heads_checked=[0, 1])
+
+
+def test_backward_many_heads_every_head_checked():
+    """16 heads, 6 history frames of 4 blocks: the history pass's 384 workgroups span all 8 XCD ranges of
+    its longest-first launch order, and every head is compared."""
+    _run(_odd(128, 128, 32, Fc=2, Fh=6, H=16, kf=3, kb=2))
+
+
+def test_backward_skewed_selection():
+    """Most query blocks name the same three history blocks and a few name their own: history tiles seen
+    by almost every query block beside tiles seen by one or none, so the launch order reorders heavily.
+    (Each list ascending, without repeats, within the selection's capacity.)"""
+    def skew(w, s):
+        sel = np.full_like(s["sel_blocks"], -1)
+        n = np.zeros_like(s["n_sel"])
+        nb, nblk = w.blocks_per_frame, w.hist_frames * w.blocks_per_frame
+        for b in range(sel.shape[0]):
+            for h in range(sel.shape[1]):
+                for qb in range(sel.shape[2]):
+                    ids = [0, 1, 2] if (qb + h) % 5 else [(3 + 7 * qb + h) % nblk, (5 + 11 * qb) % nblk]
+                    ids = sorted(set(ids))[:sel.shape[3]]
+                    sel[b, h, qb, :len(ids)] = ids
+                    n[b, h, qb] = len(ids)
+        assert nb >= 3
+        return {**s, "sel_blocks": sel, "n_sel": n}
+
+    _run(_odd(128, 256, 64, Fc=2, Fh=5, H=8, kf=2, kb=2), sel_fn=skew)
 
 
 def test_backward_selection_lists_near_lf_max_sel():
