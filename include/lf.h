@@ -266,8 +266,9 @@ lf_status lf_block_sparse_attn_fp8(const lf_geom* g, const uint8_t* q8, const ui
  * slots are left untouched; delta [B,H,Lq] is scratch the call writes
  * (rowsum(dout * out)). While the call runs, the dk_cache rows of the first
  * chunk frame of (batch 0, head 0) also hold the launch order of the
- * history pass, before their gradients are written. P and dS enter the MFMAs rounded to bf16, with
- * float32 accumulation. Same validation and error codes as the forward.
+ * history pass, before their gradients are written. P and dS enter the
+ * MFMAs rounded to bf16, with float32 accumulation. Same validation and
+ * error codes as the forward.
  * ------------------------------------------------------------------------- */
 lf_status lf_block_sparse_attn_bwd(const lf_geom* g, const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* frame_slot, const int32_t* sel_blocks, const int32_t* n_sel,
