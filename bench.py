@@ -94,11 +94,19 @@ def compress_bytes(w) -> float:
 
 
 def sources_hash(paths) -> str:
-    """First 16 hex digits of the sha256 over the files' bytes, in the given order."""
+    """First 16 hex digits of the sha256 over the files' code, in the given order: C and C++ comments and
+    blank lines are dropped and trailing spaces stripped, so an edit of comments alone keeps the hash (the
+    kernel it describes is the same)."""
+    import re
+
     h = hashlib.sha256()
     for path in paths:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -42,8 +42,11 @@
 //     taken exact branch rescales when a half's probabilities could grow too
 //     large. The normaliser sums the probabilities in float32, before they
 //     are rounded to bf16 for the PV product.
+//   * Wave priorities by stage of a tile (s_setprio): the MFMA-only chains
+//     lowest, the loops that carry the exponentials highest, so that the
+//     two wavefronts sharing a SIMD overlap softmax and matrix work.
 //   * FP8 variant (press summary section 5: FP8 with per-token activation
-//     scales; single-stage walk, D = 128): queries and keys as E4M3 codes
+//     scales; either walk, D = 128): queries and keys as E4M3 codes
 //     with E8M0 scales per 32 channels of a token, scores on the scaled FP8
 //     MFMA (32x32x64); V, P and the rest as in the bf16 walk.
 //   * Rows past the end of a ragged query block are computed on zero
