@@ -152,23 +152,38 @@ __device__ inline void store_acc_t(float* dst, const f32x16& acc, int db, int h,
   }
 }
 
-// Tile t of a query block's walk, from index t on: the current chunk's
-// KT-key tiles, then the tiles of its selected history blocks (ignored ids
-// skipped; a block is hpb = ceil(b / KT) tiles). On return t is the tile
-// found; false when the walk is over.
+// Position in a query block's walk: the current chunk's KT-key tiles
+// (frame cf, tile ct of it), then the tiles of its selected history blocks
+// (list entry e, tile half of the block; a block is hpb = ceil(b / KT)
+// tiles). Counters rather than divisions: the walk advances one tile at a
+// time.
+struct DqWalk {
+  int t = 0, cf = 0, ct = 0, e = 0, half = 0;
+};
+
+// The walk's next tile from position w.t on (ignored ids skipped): its
+// address and valid key count; false when the walk is over. On return w.t
+// is the tile found and the counters point past it.
 template <int KT>
 __device__ inline bool dq_tile(const KGeom& g, const int32_t* sel, int64_t item, int max_sel, int tpf, int n_cur,
-                               int hpb, int64_t bh, int& t, int n_tiles, int64_t& base, int& count) {
-  for (; t < n_tiles; ++t) {
+                               int hpb, int64_t bh, DqWalk& w, int n_tiles, int64_t& base, int& count) {
+  for (; w.t < n_tiles; ++w.t) {
     int slot, start;
-    if (t < n_cur) {
-      const int f2 = t / tpf, tt = t - f2 * tpf;
-      slot = g.slot[g.Fh + f2];
-      start = tt * KT;
+    if (w.t < n_cur) {
+      slot = g.slot[g.Fh + w.cf];
+      start = w.ct * KT;
       count = min(KT, g.T - start);
+      if (++w.ct == tpf) {
+        w.ct = 0;
+        ++w.cf;
+      }
     } else {
-      const int e = (t - n_cur) / hpb, half = (t - n_cur) - e * hpb;
-      const int x = sel[item * max_sel + e];
+      const int x = sel[item * max_sel + w.e];
+      const int half = w.half;
+      if (++w.half == hpb) {
+        w.half = 0;
+        ++w.e;
+      }
       if (x < 0 || x >= g.Fh * g.nb) continue;  // ignored id
       const int f = x / g.nb, jb = x - f * g.nb;
       slot = g.slot[f];
@@ -202,12 +217,21 @@ __device__ inline void dq_tile_math(const char* ks, const char* vs, int count, c
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vs, 32 * kh, st, l32, h), dof[st], dp, 0, 0, 0);
     }
     bf16x8 b0, b1;
+    if (count >= 32 * (kh + 1)) {  // every key of the half exists (wave-uniform): no mask
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool kv = 32 * kh + acc_row(r, h) < count;
-      const float p = kv ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2)) : 0.0f;
-      const __bf16 d = (__bf16)(p * (dp[r] - dd));
-      if (r < 8) b0[r] = d; else b1[r - 8] = d;
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2));
+        const __bf16 d = (__bf16)(p * (dp[r] - dd));
+        if (r < 8) b0[r] = d; else b1[r - 8] = d;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool kv = 32 * kh + acc_row(r, h) < count;
+        const float p = kv ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2)) : 0.0f;
+        const __bf16 d = (__bf16)(p * (dp[r] - dd));
+        if (r < 8) b0[r] = d; else b1[r - 8] = d;
+      }
     }
 #pragma unroll
     for (int db = 0; db < S::DB; ++db) {
@@ -283,9 +307,10 @@ __global__ __launch_bounds__(64 * WPQ, (KT == 32 && WPQ >= 2 ? 2 : 1)) void bwd_
   const int n_tiles = n_cur + len * hpb;
   TileDma<D, KT, NT> dma;
   dma.init(tid);
-  int t = 0, count = 0, ncount = 0;
+  DqWalk walk;
+  int count = 0, ncount = 0;
   int64_t nbase = 0;
-  bool have = dq_tile<KT>(g, sel, item, max_sel, tpf, n_cur, hpb, bh, t, n_tiles, nbase, ncount);
+  bool have = dq_tile<KT>(g, sel, item, max_sel, tpf, n_cur, hpb, bh, walk, n_tiles, nbase, ncount);
   if (have) {
     dma.issue(ks0, kc + nbase, ncount, tid);
     dma.issue(vs0, vc + nbase, ncount, tid);
@@ -296,8 +321,8 @@ __global__ __launch_bounds__(64 * WPQ, (KT == 32 && WPQ >= 2 ? 2 : 1)) void bwd_
 #define LF_DQ_STEP(KA, VA, KB, VB)                                                         \
   {                                                                                      \
     count = ncount;                                                                      \
-    ++t;                                                                                 \
-    const bool more = dq_tile<KT>(g, sel, item, max_sel, tpf, n_cur, hpb, bh, t, n_tiles, nbase, ncount); \
+    ++walk.t;                                                                            \
+    const bool more = dq_tile<KT>(g, sel, item, max_sel, tpf, n_cur, hpb, bh, walk, n_tiles, nbase, ncount); \
     __builtin_amdgcn_s_waitcnt(kWaitVm0);                                                \
     __syncthreads();                                                                     \
     if (more) {                                                                          \
