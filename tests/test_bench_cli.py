@@ -31,5 +31,21 @@ def test_help_lists_the_options():
     r = _bench("--help")
     assert r.returncode == 0
     for opt in ("--gpus", "--steps", "--warmup", "--workload", "--path", "--backward", "--fp8", "--headline-only",
-                "--cpu-single-thread", "--cpu-sample-qblocks", "--no-cpu-baseline", "--calibrate-copy-mib"):
+                "--cpu-single-thread", "--cpu-sample-qblocks", "--no-cpu-baseline", "--calibrate-copy-mib",
+                "--dense-vs-sdpa"):
         assert opt in r.stdout, opt
+
+
+def test_counter_traffic_follows_the_kernel_code_not_its_comments(tmp_path):
+    """The committed fabric-byte counters are reported only for the attention code they were taken on: the source
+    hash ignores comments and blank lines, and changes with any code token."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    src = tmp_path / "k.hip"
+    src.write_text("// header\nint f(int x) {  /* body */\n  return x + 1;  // done\n}\n")
+    h0 = bench.sources_hash([str(src)])
+    src.write_text("// a longer header\n\nint f(int x) {  /* other words */\n  return x + 1;\n}\n")
+    assert bench.sources_hash([str(src)]) == h0
+    src.write_text("// header\nint f(int x) {\n  return x + 2;\n}\n")
+    assert bench.sources_hash([str(src)]) != h0
