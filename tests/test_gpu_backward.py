@@ -131,6 +131,12 @@ def test_backward_skewed_selection():
     _run(_odd(128, 256, 64, Fc=2, Fh=5, H=8, kf=2, kb=2), sel_fn=skew)
 
 
+def test_backward_two_batches():
+    """B = 2, 5 heads: the history pass's launch order and the key workgroups span (batch, head) pairs of
+    both batches; every head of both is compared."""
+    _run(_odd(128, 130, 64, Fc=2, Fh=5, H=5, kf=2, kb=2).replace(batch=2, name="bwd_b2"))
+
+
 def test_backward_selection_lists_near_lf_max_sel():
     """508 selected history blocks per query block (254 frames, 2 of 4 blocks each)."""
     _run(_odd(128, 256, 64, Fc=1, Fh=254, H=1, kf=254, kb=2, n_sink=0, slots=255).replace(chunk_index=300))
