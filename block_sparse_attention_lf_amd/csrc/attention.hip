@@ -893,8 +893,8 @@ struct Walk {
 
 // SS = false: a workgroup owns 4/WPQ query blocks (128 rows) and
 // double-buffers K/V tiles (one barrier per tile). SS = true (bf16): a
-// workgroup owns one query block, holds one K and one V tile (40 KB of LDS
-// at b = 64, so four workgroups share a CU) and alternates them around two
+// workgroup owns one query block, holds one K and one V tile (34 KB of LDS
+// with its walk table at d = 128, so four workgroups share a CU) and alternates them around two
 // barriers per tile: V of tile t streams in while tile t's scores are formed,
 // K of tile t+1 while its PV products run.
 // Q8 (bf16 values, D = 128): q and k_cache are not read; the scores come

@@ -787,7 +787,7 @@ hipError_t launch_bwd_d(const KGeom& g, const void* q, const void* k, const void
   // formed once for both), with two wavefronts per SIMD (256 registers).
   // The eight-wavefront current workgroups fill a CU on their own and
   // stage up to 64 query rows per step (78 KB of LDS); the two-wavefront
-  // history workgroups stage 32 rows per step (40 KB), so four share a CU.
+  // history workgroups stage 32 rows per step (35 KB), so four share a CU.
   // The history pass runs first, in the order hist_order_kernel writes into
   // the dk rows of the first chunk frame of (batch 0, head 0): T * D floats
   // that the current-chunk pass overwrites with their gradients afterwards,
